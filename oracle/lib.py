@@ -1,0 +1,174 @@
+"""ctypes wrapper around orc.c (test infrastructure only).
+
+Builds liborc.so with gcc on first use when it is missing.  Arrays are numpy; every
+function returns fresh output arrays plus the status bits the C code reports.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+ORC_NONFINITE = 1
+ORC_SCALE_OVF = 2
+ORC_F16_OVF = 4
+ORC_BAD_AWQ = 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "orc.c")
+_LIB = os.path.join(_HERE, "liborc.so")
+_lock = threading.Lock()
+_lib = None
+
+# Strict IEEE binary32: no contraction into FMA, no fast-math, SSE scalar (x86-64 default).
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-fno-strict-aliasing", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def build(force: bool = True) -> str:
+    """Compile orc.c into liborc.so (gcc)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_U32 = ctypes.c_uint32
+
+
+def load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            lib.orc_f32_to_f16_n.argtypes = [_P, _P, _I64]
+            lib.orc_f32_to_bf16_n.argtypes = [_P, _P, _I64]
+            lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+            lib.orc_f16_to_f32.restype = ctypes.c_float
+            lib.orc_percentile_rank.argtypes = [_I64, _U32, _U32]
+            lib.orc_percentile_rank.restype = _I64
+            lib.orc_quantize_rows.argtypes = [_P, _I64, _I64, _I64, _I32, _U32, _U32, _P, _P, _P, _P, _P, _P]
+            lib.orc_quantize_rows.restype = _U32
+            lib.orc_awq_multipliers.argtypes = [_P, _I64, _P]
+            lib.orc_awq_multipliers.restype = _U32
+            lib.orc_fakequant_rows.argtypes = [_P, _I64, _I64, _I64, _I32, _U32, _U32, _P, _P, _P, _P, _P, _P]
+            lib.orc_fakequant_rows.restype = _U32
+            lib.orc_f16_passthrough.argtypes = [_P, _I64, _P]
+            lib.orc_f16_passthrough.restype = _U32
+            lib.orc_sqwa_update.argtypes = [_P, _P, _I64, _I32]
+            lib.orc_sqwa_update.restype = None
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def f32_to_f16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    load().orc_f32_to_f16_n(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    load().orc_f32_to_bf16_n(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+_F16_TABLE = None
+
+
+def f16_to_f32(h) -> np.ndarray:
+    """Exact binary16 -> binary32 through a 65536-entry table filled by orc_f16_to_f32."""
+    global _F16_TABLE
+    if _F16_TABLE is None:
+        lib = load()
+        _F16_TABLE = np.array([lib.orc_f16_to_f32(i) for i in range(65536)], dtype=np.float32)
+    return _F16_TABLE[np.ascontiguousarray(h, dtype=np.uint16)]
+
+
+def bf16_to_f32(b) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def percentile_rank(n: int, num: int, den: int) -> int:
+    return int(load().orc_percentile_rank(n, num, den))
+
+
+def quantize_rows(w, Q: int, num: int = 1, den: int = 1, awq=None, want_t: bool = False,
+                  want_clip: bool = False):
+    """Per-row quantization of a 2-D float32 array (rows x cols).
+
+    Returns dict(codes int8 [rows, cols], scales uint16 [rows], dq float32 [rows, cols],
+    status, and t / clip when asked)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    assert w.ndim == 2
+    rows, cols = w.shape
+    codes = np.empty((rows, cols), dtype=np.int8)
+    scales = np.empty(rows, dtype=np.uint16)
+    dq = np.empty((rows, cols), dtype=np.float32)
+    t = np.empty((rows, cols), dtype=np.float32) if want_t else None
+    clip = np.empty(rows, dtype=np.float32) if want_clip else None
+    a = None if awq is None else np.ascontiguousarray(awq, dtype=np.uint16)
+    if a is not None:
+        assert a.shape == (cols,)
+    st = load().orc_quantize_rows(_ptr(w), rows, cols, cols, Q, num, den, _ptr(a), _ptr(codes),
+                                  _ptr(scales), _ptr(dq), _ptr(t), _ptr(clip))
+    out = dict(codes=codes, scales=scales, dq=dq, status=int(st))
+    if want_t:
+        out["t"] = t
+    if want_clip:
+        out["clip"] = clip
+    return out
+
+
+def awq_multipliers(s):
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    a = np.empty(s.shape, dtype=np.uint16)
+    st = load().orc_awq_multipliers(_ptr(s), s.size, _ptr(a))
+    return a, int(st)
+
+
+def fakequant_rows(w_bf16, Q: int = 31, num: int = 1, den: int = 1, g_bf16=None):
+    """STE fake quantization of a 2-D bfloat16 (uint16 bits) array."""
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    rows, cols = w.shape
+    mb = (cols + 7) // 8
+    dq = np.empty((rows, cols), dtype=np.uint16)
+    scales = np.empty(rows, dtype=np.uint16)
+    mask = np.empty((rows, mb), dtype=np.uint8)
+    codes = np.empty((rows, cols), dtype=np.int8)
+    g = None if g_bf16 is None else np.ascontiguousarray(g_bf16, dtype=np.uint16)
+    g_out = None if g is None else np.empty((rows, cols), dtype=np.uint16)
+    st = load().orc_fakequant_rows(_ptr(w), rows, cols, cols, Q, num, den, _ptr(dq), _ptr(scales),
+                                   _ptr(mask), _ptr(g), _ptr(g_out), _ptr(codes))
+    return dict(dq=dq, scales=scales, mask=mask, codes=codes, g_out=g_out, status=int(st))
+
+
+def f16_passthrough(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    st = load().orc_f16_passthrough(_ptr(x), x.size, _ptr(y))
+    return y, int(st)
+
+
+def sqwa_update(mean: np.ndarray, xhat, k: int) -> np.ndarray:
+    """In-place running-mean update of a contiguous float32 array; returns it."""
+    assert mean.dtype == np.float32 and mean.flags.c_contiguous
+    xhat = np.ascontiguousarray(xhat, dtype=np.float32)
+    assert xhat.size == mean.size
+    load().orc_sqwa_update(_ptr(mean), _ptr(xhat), mean.size, k)
+    return mean
