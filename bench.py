@@ -1,0 +1,186 @@
+"""Throughput of the per-row weight quantizer on one MI355X.
+
+One step = one whole-model export of the 9-layer d=512 GPT weight set (21,767,168 fp32
+parameters in 64 tensors): int6 per-row codes with the clip at the 99.99th percentile of
+|w| per row, int8 absmax for tok_emb.weight, fp16 passthrough for the 18 vectors, fp16
+row scales and the fp32 dequantized weights.  That is every step of the path in one
+grouped launch (load, clip, scale, round, clamp, dequant, export dispatch).
+
+Inputs are seeded synthetic N(0, 0.02^2) weights, resident in HBM before timing.  Several
+independent copies of the inputs and outputs are used in rotation, so that no step finds
+its data in the 256 MiB Infinity Cache.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantizer GB/s (bytes in+out) and % of MI355X HBM peak, int6 per-row"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["int6_weight_export_amd/csrc/pgq_kernels.hip", "int6_weight_export_amd/csrc/pgq_api.hip",
+                  "int6_weight_export_amd/csrc/pgq_desc.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_export_gpt9.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(tensors, want_dq: bool) -> dict:
+    """Bytes each launch must move at least once: inputs read, outputs written."""
+    import oracle
+
+    pol = oracle.Policy()
+    b_in = b_codes = b_scales = b_f16 = b_dq = 0
+    rows_total = 0
+    for t in tensors:
+        kind = oracle.tensor_kind(t.name, t.numel, pol)
+        rows, cols = oracle.as_rows(t.shape)
+        b_in += 4 * t.numel
+        if kind == oracle.KIND_F16:
+            b_f16 += 2 * t.numel
+        else:
+            b_codes += t.numel
+            b_scales += 2 * rows
+            rows_total += rows
+        if want_dq:
+            b_dq += 4 * t.numel
+    total = b_in + b_codes + b_scales + b_f16 + b_dq
+    return dict(total=total, read=b_in, write=total - b_in, rows=rows_total)
+
+
+def cpu_baseline(tensors, min_seconds: float = 10.0, max_passes: int = 4) -> dict:
+    """The oracle (single-threaded C) on the same weight set, whole export passes."""
+    import oracle
+
+    pol = oracle.Policy()
+    data = [(t.name, t.data) for t in tensors]
+    nbytes = algorithmic_bytes(tensors, want_dq=True)["total"]
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.export(data, pol)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or passes >= max_passes:
+            break
+    return {"value": round(nbytes * passes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full export pass(es) of the same 9-layer weight set with fp32 dequant "
+                      f"({el:.1f} s, single thread)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--copies", type=int, default=6, help="input/output sets used in rotation")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer is "
+              f"row-parallel within a GPU and this build runs no collectives)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from int6_weight_export_amd import ops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    tensors = synth.config2()
+    ab = algorithmic_bytes(tensors, want_dq=True)
+
+    sets = []
+    for c in range(args.copies):
+        dts = [ops.ExportTensor(t.name, torch.from_numpy(t.data).to("cuda")) for t in tensors]
+        ex = ops.Exporter(dts, want_dq=True)
+        ex.run()                                  # uploads the descriptor table once
+        sets.append(ex)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        sets[i % len(sets)].run()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        sets[i % len(sets)].run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    status = [int(s.status.item()) for s in sets]
+    assert all(x == 0 for x in status), status
+
+    ms_per_step = wall / args.steps * 1e3
+    value = ab["total"] / (wall / args.steps) / 1e9
+    k_avg_s = float(np.mean(kern_ms)) / 1e3
+    achieved = ab["total"] / k_avg_s / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256") == kernel_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "whole-model export of the 9-layer d=512 GPT weight set: int6 per-row codes with "
+                        "99.99th-percentile clip, int8 tok_emb.weight, fp16 passthrough vectors, fp16 row "
+                        "scales, fp32 dequantized weights",
+            "tensors": len(tensors),
+            "params": int(sum(t.numel for t in tensors)),
+            "bytes_per_step": ab["total"],
+            "rows_per_step": ab["rows"],
+            "input_copies_in_rotation": args.copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernel_us_avg": round(k_avg_s * 1e6, 3),
+        "kernel_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+                              round(float(np.percentile(kern_ms, 90)) * 1e3, 3)],
+        "rows_per_s": round(ab["rows"] / (wall / args.steps), 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(tensors)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

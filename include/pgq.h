@@ -1,0 +1,213 @@
+/*
+ * pgq.h -- per-row symmetric weight quantization on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpgq.so.  Plain pointers and sizes only.  Every data pointer below is a
+ * DEVICE pointer on the current HIP device unless the comment says "host".  `stream`
+ * is a hipStream_t passed as void* (NULL = the default stream).  All calls are
+ * asynchronous on `stream`; none synchronizes it.
+ *
+ * What is computed (Parameter Golf submission pages):
+ *   - per-row quantization, percentile clipping for export and small-tensor FP16
+ *     passthrough: "Swiglu gating ... 10min/16MB Track" (PR #2159), list "Key Explored
+ *     Modifications";
+ *   - 6-bit codes in [-31, 31] and STE fake quantization in the forward pass: "SubSixteen
+ *     v2: Int6 QAT + MLP 3x + SWA" card (PR #69), sections Quantization and Other;
+ *   - int8 for the tensors named by QUANT_INT8_NAME_PATTERNS (default tok_emb.weight,
+ *     lm_head.weight) and int6 AWQ export: "12L 24min Vocab1792 ... Int6AWQ MixedBits"
+ *     (PR #1495), Submission summary and Mixed-bit quantization details;
+ *   - averaging of quantize-dequantize snapshots (SQWA): "Discriminative TTT + SLOT-24"
+ *     card (PR #1414), Novel Contributions.
+ *
+ * The arithmetic, fixed where the pages leave it open (Q = 2^(bits-1) - 1, every step an
+ * IEEE binary32 operation with round-to-nearest-even):
+ *   x_j   = w_j                         (AWQ: x_j = w_j * a_j,  a_j = fp16(sqrt(s_j)))
+ *   clip  = k-th smallest |x_j|, k = ceil(pct_num * n / pct_den) clamped to [1, n]
+ *   s     = fp16(clip / Q); s = 1.0 when that rounds to zero
+ *   t_j   = x_j / s;  code_j = clamp(rne(t_j), -Q, Q)
+ *   dq_j  = code_j * s                  (AWQ: dq_j = (code_j * s) / a_j)
+ *   STE:  mask_j = |t_j| <= Q + 1/2;  grad_out_j = mask_j ? grad_j : +0
+ *   SQWA: mean = xhat (k = 1), mean = mean + (xhat - mean) / k (k > 1)
+ *
+ * Errors.  Argument errors return a pgq_status synchronously and enqueue nothing.
+ * Conditions that depend on the data (NaN/Inf inputs, scale or fp16 overflow, bad AWQ
+ * scales, a stale descriptor table) are OR-ed into *dev_status on the device with an
+ * atomic; the library never clears that word.  Outputs of an affected row are
+ * unspecified.
+ *
+ * Ownership.  The caller allocates every device buffer and keeps it alive until the
+ * stream work that uses it has completed.  The library allocates no device memory and
+ * keeps no state besides a per-device cache of launch limits; it is thread-safe.  Host
+ * arrays are read during the call only.  Inputs and outputs must not overlap, except
+ * that `mean` is updated in place.
+ */
+#ifndef PGQ_H
+#define PGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PGQ_OK = 0,
+    PGQ_ERR_NULL = 1,       /* a required pointer is NULL */
+    PGQ_ERR_SHAPE = 2,      /* negative size, ld < cols, too many rows */
+    PGQ_ERR_DTYPE = 3,      /* unsupported element type for this call */
+    PGQ_ERR_PARAM = 4,      /* bits outside [2, 8], pct_den == 0 or pct_num > pct_den, bad mode/k/kind */
+    PGQ_ERR_ALIGN = 5,      /* pointer not aligned to its element size */
+    PGQ_ERR_WORKSPACE = 6,  /* workspace missing or smaller than required */
+    PGQ_ERR_HIP = 7         /* a HIP runtime call or kernel launch failed */
+} pgq_status;
+
+/* Bits OR-ed into *dev_status by the kernels. */
+#define PGQ_DEV_NONFINITE   1u   /* a NaN or infinity in an input row */
+#define PGQ_DEV_SCALE_OVF   2u   /* clip / Q rounds to fp16 infinity (clip >= 65520 * Q) */
+#define PGQ_DEV_F16_OVF     4u   /* an fp16 passthrough value rounded to infinity */
+#define PGQ_DEV_BAD_AWQ     8u   /* an AWQ activation scale is <= 0 or not finite */
+#define PGQ_DEV_STALE_TABLE 16u  /* PGQ_TABLE_RESIDENT given but the workspace holds another table; nothing was written */
+
+/* Element types. */
+#define PGQ_F32  0
+#define PGQ_BF16 1
+
+/* Export kinds: an integer kind is its bit width; PGQ_KIND_F16 is fp16 passthrough. */
+#define PGQ_KIND_F16 16
+
+/* Flags for the grouped calls. */
+#define PGQ_TABLE_RESIDENT 1u    /* the workspace already holds the descriptor table that an earlier
+                                    call of the same entry point wrote for identical arguments: skip
+                                    the upload.  The kernels compare a checksum of the table with the
+                                    one this call computes and write nothing if they differ
+                                    (PGQ_DEV_STALE_TABLE). */
+
+/* Quantizer parameters: code width and the clip percentile pct_num / pct_den
+ * (1/1 = absolute maximum; 9999/10000 = 99.99th percentile). */
+typedef struct {
+    int32_t bits;       /* 2..8; Q = 2^(bits-1) - 1 (6 -> 31, 8 -> 127) */
+    uint32_t pct_num;   /* 0 <= pct_num <= pct_den */
+    uint32_t pct_den;   /* > 0 */
+} pgq_qparams;
+
+/* ------------------------------------------------------------------------------------------ */
+/* One matrix.                                                                                  */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Quantize each row of a rows x cols matrix (row stride ld elements, ld >= cols).
+ *   w         input, PGQ_F32 or PGQ_BF16 (w_dtype)
+ *   awq_s     NULL, or cols fp32 activation scales s_j > 0: the row is multiplied by
+ *             a_j = fp16(sqrt(s_j)) before quantization and divided by it in dequant
+ *   awq_mult  NULL, or cols fp16 outputs (bit patterns) receiving a_j
+ *   codes     NULL, or rows x cols int8 codes (row stride cols)
+ *   scales    rows fp16 scales (bit patterns); required
+ *   dq        NULL, or rows x cols dequantized values (row stride cols) of type dq_dtype
+ * Source: per-row quantization and percentile clipping (PR #2159, Key Explored
+ * Modifications); range [-31, 31] for 6 bits (PR #69 card, section Other); int6 AWQ
+ * export (PR #1495, Submission summary). */
+pgq_status pgq_quantize_rows(const void* w, int32_t w_dtype, int64_t rows, int64_t cols, int64_t ld,
+                             pgq_qparams qp, const float* awq_s, uint16_t* awq_mult,
+                             int8_t* codes, uint16_t* scales, void* dq, int32_t dq_dtype,
+                             uint32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* STE fake quantization for quantization-aware training (grouped over n bf16 matrices).       */
+/* Source: PR #69 card, section Other (straight-through estimator fake quantization in the     */
+/* forward pass, range [-31, 31]) and section Quantization (STE QAT, 6 bits).                  */
+/* ------------------------------------------------------------------------------------------ */
+
+#define PGQ_FQ_FWD     1   /* w -> dq, scales, mask (and codes) */
+#define PGQ_FQ_BWD     2   /* mask, grad -> grad_out */
+#define PGQ_FQ_FWD_BWD 3   /* both, in one pass over w and grad */
+
+typedef struct {
+    const uint16_t* w;      /* bf16 weights, rows x cols, row stride ld (FWD, FWD_BWD) */
+    int64_t rows, cols, ld;
+    uint16_t* dq;           /* bf16 fp32->bf16(code * s), rows x cols dense (FWD, FWD_BWD) */
+    uint16_t* scales;       /* fp16, rows (FWD, FWD_BWD) */
+    uint8_t* mask;          /* rows x ceil(cols/8) bytes, bit j%8 of byte j/8 = mask_j.  Written by
+                               FWD and FWD_BWD (may be NULL there), read by BWD */
+    const uint16_t* grad;   /* bf16 upstream gradient, rows x cols dense (BWD, FWD_BWD) */
+    uint16_t* grad_out;     /* bf16 masked gradient, rows x cols dense (BWD, FWD_BWD) */
+    int8_t* codes;          /* NULL or rows x cols int8 codes (FWD, FWD_BWD) */
+} pgq_fq_tensor;
+
+/* Workspace bytes the grouped fake-quant call needs for these n tensors. */
+pgq_status pgq_fakequant_workspace(const pgq_fq_tensor* t, int32_t n, size_t* workspace_bytes);
+
+/* mode: PGQ_FQ_*.  t: host array of n descriptors.  workspace: device scratch of at least
+ * pgq_fakequant_workspace() bytes (may be NULL when n == 1).  flags: 0 or PGQ_TABLE_RESIDENT. */
+pgq_status pgq_fakequant_fwd_bwd(int32_t mode, const pgq_fq_tensor* t, int32_t n, pgq_qparams qp,
+                                 void* workspace, size_t workspace_bytes, uint32_t flags,
+                                 uint32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Whole-model export (one grouped launch over every tensor).                                  */
+/* Source: PR #2159 Key Explored Modifications (per-row quantization, percentile clipping,     */
+/* small-tensor FP16 passthrough); PR #1495 Mixed-bit quantization details (int6 by default,   */
+/* int8 for names matching QUANT_INT8_NAME_PATTERNS) and Submission summary (int6 AWQ).        */
+/* ------------------------------------------------------------------------------------------ */
+
+typedef struct {
+    const char* name;       /* host string used by the policy (NULL = "") */
+    const void* w;          /* device input, rows x cols, row stride ld */
+    int32_t dtype;          /* PGQ_F32 or PGQ_BF16 */
+    int32_t reserved;
+    int64_t rows, cols, ld; /* 1-D tensors: rows = 1; higher ranks: rows = shape[0] */
+    const float* awq_s;     /* NULL or cols fp32 activation scales (used for integer kinds whose
+                               bits equal the policy's default bits) */
+} pgq_tensor_in;
+
+typedef struct {
+    const char* const* int8_patterns; /* host array of n_patterns host strings; a tensor whose name
+                                         contains one of them (substring) uses q_sensitive */
+    int32_t n_patterns;
+    int32_t reserved;
+    int64_t passthrough_below;        /* tensors with fewer elements are stored as fp16 (65536) */
+    pgq_qparams q_default;            /* e.g. {6, 9999, 10000} */
+    pgq_qparams q_sensitive;          /* e.g. {8, 1, 1} */
+} pgq_policy;
+
+typedef struct {
+    int32_t kind;           /* PGQ_KIND_F16, or the code width in bits */
+    int32_t has_awq;        /* 1 when AWQ multipliers are produced for this tensor */
+    pgq_qparams qp;         /* quantizer of an integer kind */
+    int64_t codes_off;      /* byte offsets into the arena; -1 when absent */
+    int64_t scales_off;
+    int64_t f16_off;
+    int64_t awq_off;
+} pgq_tensor_plan;
+
+/* Host only (no device work): decide each tensor's kind and lay out the output arena.
+ * plan: host array of n entries (written).  arena_bytes / workspace_bytes: sizes the
+ * caller must allocate for pgq_export_model / pgq_sqwa_accumulate.  Regions are 256-byte
+ * aligned: codes rows x cols int8, scales rows fp16, f16 numel fp16, awq cols fp16. */
+pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* pol,
+                           pgq_tensor_plan* plan, size_t* arena_bytes, size_t* workspace_bytes);
+
+/* Quantize every tensor into the arena in one launch.  dq_out: NULL, or a host array of n
+ * device pointers (each NULL or rows x cols fp32) receiving the value each tensor decodes to
+ * (code * s, AWQ-divided, or fp32(fp16) for passthrough). */
+pgq_status pgq_export_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan* plan,
+                            void* arena, float* const* dq_out, void* workspace, size_t workspace_bytes,
+                            uint32_t flags, uint32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* SQWA: fold snapshot k (1-based) into per-tensor fp32 running means.                         */
+/* Source: "Discriminative TTT + SLOT-24" card (PR #1414), Novel Contributions: average        */
+/* quantize-dequantize snapshots.  Each snapshot tensor is quantized and dequantized with the  */
+/* plan's kind (fp16 round trip for passthrough), then mean = xhat (k = 1) or                  */
+/* mean + (xhat - mean) / k.  Export the final mean with pgq_export_model and the same plan.   */
+/* ------------------------------------------------------------------------------------------ */
+pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_tensor_plan* plan,
+                               float* const* mean, int32_t k, void* workspace, size_t workspace_bytes,
+                               uint32_t flags, uint32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+const char* pgq_status_str(pgq_status s);   /* static string */
+const char* pgq_version(void);              /* static string */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PGQ_H */

@@ -1,0 +1,529 @@
+// pgq_api.hip -- host layer of libpgq: argument checks, export planning, descriptor
+// tables and launches behind the C ABI declared in include/pgq.h.
+//
+// Argument errors return before anything is enqueued.  Grouped calls write one table
+// (header + per-tensor descriptors + row tiles) into the caller's workspace with one
+// host-to-device copy on the caller's stream, unless PGQ_TABLE_RESIDENT says the same
+// table is already there; the kernels verify its checksum either way.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "pgq_desc.h"
+#include "../../include/pgq.h"
+
+using namespace pgq;
+
+namespace {
+
+int env_int(const char* name, int dflt, int lo, int hi)
+{
+    const char* v = getenv(name);
+    if (!v || !*v) return dflt;
+    int x = atoi(v);
+    return std::min(std::max(x, lo), hi);
+}
+
+// Rows per wavefront in one tile (a tile is kWaves * rows_per_wave rows of one tensor).
+int rows_per_wave()
+{
+    static const int v = env_int("PGQ_ROWS_PER_WAVE", 2, 1, 64);
+    return v;
+}
+
+// Resident workgroups per compute unit for the persistent grid (0 = from the occupancy API).
+int wg_per_cu_override()
+{
+    static const int v = env_int("PGQ_WG_PER_CU", 0, 0, 64);
+    return v;
+}
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool qparams_ok(const pgq_qparams& q)
+{
+    return q.bits >= 2 && q.bits <= 8 && q.pct_den > 0 && q.pct_num <= q.pct_den;
+}
+
+// The clip is the k-th smallest |x| with k = ceil(num * n / den) in [1, n]; kernels use
+// its rank from the top, n - k + 1.
+int64_t rank_top(int64_t n, uint32_t num, uint32_t den)
+{
+    if (n <= 0) return 1;
+    unsigned __int128 p = (unsigned __int128)num * (unsigned __int128)n;
+    int64_t k = (int64_t)((p + den - 1) / den);
+    k = std::min(std::max<int64_t>(k, 1), n);
+    return n - k + 1;
+}
+
+// 64-bit hash of a table (multiply-xorshift over 8-byte words; n is a multiple of 8).
+uint64_t table_hash(const void* data, size_t n, uint64_t h)
+{
+    const uint8_t* p = static_cast<const uint8_t*>(data);
+    for (size_t i = 0; i + 8 <= n; i += 8) {
+        uint64_t w;
+        memcpy(&w, p + i, 8);
+        h = (h ^ w) * 0x9E3779B97F4A7C15ull;
+        h ^= h >> 29;
+    }
+    return h;
+}
+
+size_t esize(int32_t dt) { return dt == PGQ_F32 ? 4 : 2; }
+
+bool shape_ok(int64_t rows, int64_t cols, int64_t ld)
+{
+    if (rows < 0 || cols < 0 || ld < cols) return false;
+    if (cols > ((int64_t)1 << 31) - 64) return false;           // per-row counters are 32-bit
+    if (rows > ((int64_t)1 << 32) - 1) return false;            // tile row origins are 32-bit
+    return true;
+}
+
+// Vector (16-byte) path: every stream of this tensor is aligned to its vector width.
+void set_vec_flag(Desc& d)
+{
+    const int vec = d.in_dtype == IN_F32 ? 4 : 8;
+    const size_t ein = d.in_dtype == IN_F32 ? 4 : 2;
+    bool ok = d.cols % vec == 0 && d.ld % vec == 0 && aligned(d.w, 16);
+    const size_t dqe = d.dq_dtype == IN_F32 ? 4 : 2;
+    ok = ok && (!d.codes || aligned(d.codes, vec));
+    ok = ok && (!d.dq || aligned(d.dq, std::min<size_t>(16, vec * dqe)));
+    ok = ok && (!d.awq_s || aligned(d.awq_s, 16));
+    ok = ok && (!d.awq_out || aligned(d.awq_out, vec * 2));
+    ok = ok && (!d.f16_out || aligned(d.f16_out, vec * 2));
+    ok = ok && (!d.mean || aligned(d.mean, 16));
+    ok = ok && (!d.grad || aligned(d.grad, 16));
+    ok = ok && (!d.grad_out || aligned(d.grad_out, 16));
+    (void)ein;
+    d.flags = ok ? DF_VEC : 0u;
+}
+
+Desc blank_desc()
+{
+    Desc d;
+    memset(&d, 0, sizeof(d));
+    d.rank_top = 1;
+    return d;
+}
+
+struct LimitCache {
+    std::mutex mu;
+    // [device][mode*4+awq*2+sel] -> resident blocks per CU; n_cu per device
+    std::vector<std::vector<int>> per_cu;
+    std::vector<int> n_cu;
+};
+LimitCache g_limits;
+
+uint32_t grid_for(int mode, bool awq, bool sel, uint32_t n_tiles)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    int per_cu = 0, ncu = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_limits.mu);
+        if ((int)g_limits.per_cu.size() <= dev) {
+            g_limits.per_cu.resize(dev + 1, std::vector<int>(16, -1));
+            g_limits.n_cu.resize(dev + 1, -1);
+        }
+        int& slot = g_limits.per_cu[dev][mode * 4 + (awq ? 2 : 0) + (sel ? 1 : 0)];
+        if (slot < 0 || g_limits.n_cu[dev] < 0) {
+            int pc = 0, nc = 0;
+            if (max_resident_blocks(mode, awq, sel, &pc, &nc) != 0 || pc <= 0 || nc <= 0) { pc = 4; nc = 256; }
+            slot = pc;
+            g_limits.n_cu[dev] = nc;
+        }
+        per_cu = slot;
+        ncu = g_limits.n_cu[dev];
+    }
+    const int ov = wg_per_cu_override();
+    if (ov > 0) per_cu = ov;
+    const uint64_t g = (uint64_t)per_cu * (uint64_t)ncu;
+    return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(g, n_tiles));
+}
+
+size_t table_bytes(size_t n_desc)
+{
+    return sizeof(TableHeader) + align_up((int64_t)(n_desc * sizeof(Desc)), 64) +
+           (size_t)align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 8);
+}
+
+uint64_t tiles_for(int64_t rows)
+{
+    const int64_t rpb = (int64_t)kWaves * rows_per_wave();
+    return rows > 0 ? (uint64_t)((rows + rpb - 1) / rpb) : 0;
+}
+
+// Build the table on the host, upload it (unless resident) and launch one grouped kernel.
+pgq_status run_grouped(int mode, bool awq, const std::vector<Desc>& descs, void* ws, size_t ws_bytes,
+                       uint32_t flags, uint32_t* dev_status, int sqwa_k, int fq_mode, void* stream)
+{
+    const size_t n = descs.size();
+    std::vector<uint32_t> start(n + 1, 0);
+    uint64_t total = 0;
+    for (size_t i = 0; i < n; ++i) {
+        start[i] = (uint32_t)total;
+        if (descs[i].cols > 0) total += tiles_for(descs[i].rows);
+        if (total > 0xFFFFFFF0ull) return PGQ_ERR_SHAPE;
+    }
+    start[n] = (uint32_t)total;
+    if (total == 0) return PGQ_OK;
+    const size_t need = table_bytes(n);
+    if (!ws) return PGQ_ERR_WORKSPACE;
+    if (ws_bytes < need) return PGQ_ERR_WORKSPACE;
+    if (!aligned(ws, 64)) return PGQ_ERR_ALIGN;
+
+    std::vector<uint64_t> buf8((need + 7) / 8, 0);
+    uint8_t* buf = reinterpret_cast<uint8_t*>(buf8.data());
+    TableHeader* hdr = reinterpret_cast<TableHeader*>(buf);
+    const size_t desc_off = sizeof(TableHeader);
+    const size_t start_off = desc_off + align_up((int64_t)(n * sizeof(Desc)), 64);
+    memcpy(buf + desc_off, descs.data(), n * sizeof(Desc));
+    memcpy(buf + start_off, start.data(), (n + 1) * sizeof(uint32_t));
+    uint64_t h = table_hash(buf + desc_off, need - desc_off, 0x243F6A8885A308D3ull ^ (uint64_t)mode);
+    h = table_hash(&total, 8, h ^ (uint64_t)rows_per_wave());
+    hdr->magic = kTableMagic;
+    hdr->checksum = h;
+    hdr->n_desc = (uint32_t)n;
+    hdr->n_tiles = (uint32_t)total;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!(flags & PGQ_TABLE_RESIDENT)) {
+        // A pageable source is staged by the runtime before this call returns.
+        if (hipMemcpyAsync(ws, buf, need, hipMemcpyHostToDevice, s) != hipSuccess) return PGQ_ERR_HIP;
+    }
+    KArgs ka;
+    memset(&ka, 0, sizeof(ka));
+    ka.hdr = static_cast<const TableHeader*>(ws);
+    ka.table = reinterpret_cast<const Desc*>(static_cast<const uint8_t*>(ws) + desc_off);
+    ka.tile_start = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(ws) + start_off);
+    ka.checksum = h;
+    ka.status = dev_status;
+    ka.n_tiles = (uint32_t)total;
+    ka.rows_per_wave = rows_per_wave();
+    ka.sqwa_k = sqwa_k;
+    ka.fq_mode = fq_mode;
+    ka.single = blank_desc();
+    bool sel = false;
+    for (const Desc& d : descs) sel = sel || (d.rank_top > 1 && d.kind != KIND_F16);
+    const uint32_t grid = grid_for(mode, awq, sel, ka.n_tiles);
+    if (launch(mode, awq, sel, ka, grid, stream) != 0) return PGQ_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return PGQ_ERR_HIP;
+    return PGQ_OK;
+}
+
+pgq_status run_single(int mode, bool awq, const Desc& d, uint32_t* dev_status, int sqwa_k, int fq_mode,
+                      void* stream)
+{
+    if (d.rows <= 0 || d.cols <= 0) return PGQ_OK;
+    KArgs ka;
+    memset(&ka, 0, sizeof(ka));
+    ka.status = dev_status;
+    ka.rows_per_wave = rows_per_wave();
+    const uint64_t nt = tiles_for(d.rows);
+    if (nt > 0xFFFFFFFFull) return PGQ_ERR_SHAPE;
+    ka.n_tiles = (uint32_t)nt;
+    ka.sqwa_k = sqwa_k;
+    ka.fq_mode = fq_mode;
+    ka.single = d;
+    const bool sel = d.rank_top > 1;
+    const uint32_t grid = grid_for(mode, awq, sel, ka.n_tiles);
+    if (launch(mode, awq, sel, ka, grid, stream) != 0) return PGQ_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return PGQ_ERR_HIP;
+    return PGQ_OK;
+}
+
+bool name_matches(const char* name, const pgq_policy* pol)
+{
+    const char* nm = name ? name : "";
+    for (int32_t i = 0; i < pol->n_patterns; ++i) {
+        const char* p = pol->int8_patterns[i];
+        if (p && *p && strstr(nm, p)) return true;
+    }
+    return false;
+}
+
+pgq_status check_tensor_in(const pgq_tensor_in& t)
+{
+    if (!shape_ok(t.rows, t.cols, t.ld)) return PGQ_ERR_SHAPE;
+    if (t.dtype != PGQ_F32 && t.dtype != PGQ_BF16) return PGQ_ERR_DTYPE;
+    if (t.rows > 0 && t.cols > 0 && !t.w) return PGQ_ERR_NULL;
+    if (t.w && !aligned(t.w, esize(t.dtype))) return PGQ_ERR_ALIGN;
+    if (t.awq_s && !aligned(t.awq_s, 4)) return PGQ_ERR_ALIGN;
+    return PGQ_OK;
+}
+
+pgq_status check_plan_entry(const pgq_tensor_plan& p)
+{
+    if (p.kind == PGQ_KIND_F16) return PGQ_OK;
+    if (p.kind < 2 || p.kind > 8 || p.qp.bits != p.kind || !qparams_ok(p.qp)) return PGQ_ERR_PARAM;
+    return PGQ_OK;
+}
+
+// Descriptor of one export / SQWA tensor from its input and plan entry.
+pgq_status export_desc(const pgq_tensor_in& t, const pgq_tensor_plan& p, uint8_t* arena, Desc& d)
+{
+    d = blank_desc();
+    d.w = t.w;
+    d.rows = t.rows;
+    d.cols = t.cols;
+    d.ld = t.ld;
+    d.in_dtype = t.dtype == PGQ_F32 ? IN_F32 : IN_BF16;
+    d.dq_dtype = IN_F32;
+    const int64_t numel = t.rows * t.cols;
+    if (p.kind == PGQ_KIND_F16) {
+        d.kind = KIND_F16;
+        if (arena && numel > 0) {
+            if (p.f16_off < 0) return PGQ_ERR_PARAM;
+            d.f16_out = reinterpret_cast<uint16_t*>(arena + p.f16_off);
+        }
+    } else {
+        d.kind = p.kind;
+        d.Q = (1 << (p.kind - 1)) - 1;
+        d.rank_top = rank_top(t.cols, p.qp.pct_num, p.qp.pct_den);
+        if (arena && numel > 0) {
+            if (p.codes_off < 0 || p.scales_off < 0) return PGQ_ERR_PARAM;
+            d.codes = reinterpret_cast<int8_t*>(arena + p.codes_off);
+            d.scales = reinterpret_cast<uint16_t*>(arena + p.scales_off);
+        }
+        if (p.has_awq) {
+            if (!t.awq_s) return PGQ_ERR_NULL;
+            d.awq_s = t.awq_s;
+            if (arena && numel > 0) {
+                if (p.awq_off < 0) return PGQ_ERR_PARAM;
+                d.awq_out = reinterpret_cast<uint16_t*>(arena + p.awq_off);
+            }
+        }
+    }
+    return PGQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pgq_version(void) { return "pgq 0.1 (gfx950)"; }
+
+const char* pgq_status_str(pgq_status s)
+{
+    switch (s) {
+    case PGQ_OK: return "ok";
+    case PGQ_ERR_NULL: return "required pointer is NULL";
+    case PGQ_ERR_SHAPE: return "invalid shape (negative size, ld < cols, or too large)";
+    case PGQ_ERR_DTYPE: return "unsupported element type";
+    case PGQ_ERR_PARAM: return "invalid parameter (bits, percentile, mode, k or plan kind)";
+    case PGQ_ERR_ALIGN: return "pointer not aligned to its element size";
+    case PGQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case PGQ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+pgq_status pgq_quantize_rows(const void* w, int32_t w_dtype, int64_t rows, int64_t cols, int64_t ld,
+                             pgq_qparams qp, const float* awq_s, uint16_t* awq_mult,
+                             int8_t* codes, uint16_t* scales, void* dq, int32_t dq_dtype,
+                             uint32_t* dev_status, void* stream)
+{
+    if (!shape_ok(rows, cols, ld)) return PGQ_ERR_SHAPE;
+    if (w_dtype != PGQ_F32 && w_dtype != PGQ_BF16) return PGQ_ERR_DTYPE;
+    if (dq && dq_dtype != PGQ_F32 && dq_dtype != PGQ_BF16) return PGQ_ERR_DTYPE;
+    if (!qparams_ok(qp)) return PGQ_ERR_PARAM;
+    if (rows == 0) return PGQ_OK;
+    if (cols == 0) return PGQ_ERR_SHAPE;
+    if (!w || !scales) return PGQ_ERR_NULL;
+    if (awq_mult && !awq_s) return PGQ_ERR_NULL;
+    if (!aligned(w, esize(w_dtype)) || !aligned(scales, 2) || (dq && !aligned(dq, esize(dq_dtype))) ||
+        (awq_s && !aligned(awq_s, 4)) || (awq_mult && !aligned(awq_mult, 2)))
+        return PGQ_ERR_ALIGN;
+    Desc d = blank_desc();
+    d.w = w;
+    d.codes = codes;
+    d.scales = scales;
+    d.dq = dq;
+    d.awq_s = awq_s;
+    d.awq_out = awq_mult;
+    d.rows = rows;
+    d.cols = cols;
+    d.ld = ld;
+    d.kind = qp.bits;
+    d.Q = (1 << (qp.bits - 1)) - 1;
+    d.rank_top = rank_top(cols, qp.pct_num, qp.pct_den);
+    d.in_dtype = w_dtype == PGQ_F32 ? IN_F32 : IN_BF16;
+    d.dq_dtype = dq_dtype == PGQ_F32 ? IN_F32 : IN_BF16;
+    set_vec_flag(d);
+    return run_single(MODE_EXPORT, awq_s != nullptr, d, dev_status, 0, 0, stream);
+}
+
+pgq_status pgq_fakequant_workspace(const pgq_fq_tensor* t, int32_t n, size_t* workspace_bytes)
+{
+    if (!workspace_bytes) return PGQ_ERR_NULL;
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (n > 0 && !t) return PGQ_ERR_NULL;
+    for (int32_t i = 0; i < n; ++i)
+        if (!shape_ok(t[i].rows, t[i].cols, t[i].ld)) return PGQ_ERR_SHAPE;
+    *workspace_bytes = table_bytes((size_t)n);
+    return PGQ_OK;
+}
+
+pgq_status pgq_fakequant_fwd_bwd(int32_t mode, const pgq_fq_tensor* t, int32_t n, pgq_qparams qp,
+                                 void* workspace, size_t workspace_bytes, uint32_t flags,
+                                 uint32_t* dev_status, void* stream)
+{
+    if (mode != PGQ_FQ_FWD && mode != PGQ_FQ_BWD && mode != PGQ_FQ_FWD_BWD) return PGQ_ERR_PARAM;
+    if (!qparams_ok(qp)) return PGQ_ERR_PARAM;
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (n == 0) return PGQ_OK;
+    if (!t) return PGQ_ERR_NULL;
+    const bool fwd = mode & PGQ_FQ_FWD, bwd = mode & PGQ_FQ_BWD;
+    std::vector<Desc> descs((size_t)n);
+    for (int32_t i = 0; i < n; ++i) {
+        const pgq_fq_tensor& x = t[i];
+        if (!shape_ok(x.rows, x.cols, x.ld)) return PGQ_ERR_SHAPE;
+        if (x.rows > 0 && x.cols == 0) return PGQ_ERR_SHAPE;
+        Desc& d = descs[i];
+        d = blank_desc();
+        d.rows = x.rows;
+        d.cols = x.cols;
+        d.ld = x.ld;
+        d.kind = qp.bits;
+        d.Q = (1 << (qp.bits - 1)) - 1;
+        d.rank_top = rank_top(x.cols, qp.pct_num, qp.pct_den);
+        d.in_dtype = IN_BF16;
+        d.dq_dtype = IN_BF16;
+        if (x.rows == 0) continue;
+        if (fwd) {
+            if (!x.w || !x.dq || !x.scales) return PGQ_ERR_NULL;
+            d.w = x.w;
+            d.dq = x.dq;
+            d.scales = x.scales;
+            d.codes = x.codes;
+            d.mask = x.mask;
+        } else {
+            if (!x.mask) return PGQ_ERR_NULL;
+            d.mask = x.mask;
+            d.ld = x.cols;
+        }
+        if (bwd) {
+            if (!x.grad || !x.grad_out) return PGQ_ERR_NULL;
+            d.grad = x.grad;
+            d.grad_out = x.grad_out;
+        }
+        if ((d.w && !aligned(d.w, 2)) || (d.dq && !aligned(d.dq, 2)) || (d.scales && !aligned(d.scales, 2)) ||
+            (d.grad && !aligned(d.grad, 2)) || (d.grad_out && !aligned(d.grad_out, 2)))
+            return PGQ_ERR_ALIGN;
+        if (fwd) {
+            set_vec_flag(d);
+        } else {
+            const bool ok = d.cols % 8 == 0 && aligned(d.grad, 16) && aligned(d.grad_out, 16);
+            d.flags = ok ? DF_VEC : 0u;
+        }
+    }
+    const int kmode = fwd ? MODE_FQ : MODE_FQ_BWD;
+    if (n == 1 && !workspace) return run_single(kmode, false, descs[0], dev_status, 0, mode, stream);
+    return run_grouped(kmode, false, descs, workspace, workspace_bytes, flags, dev_status, 0, mode, stream);
+}
+
+pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* pol,
+                           pgq_tensor_plan* plan, size_t* arena_bytes, size_t* workspace_bytes)
+{
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (!pol || !arena_bytes || !workspace_bytes || (n > 0 && (!t || !plan))) return PGQ_ERR_NULL;
+    if (pol->n_patterns < 0 || (pol->n_patterns > 0 && !pol->int8_patterns)) return PGQ_ERR_PARAM;
+    if (!qparams_ok(pol->q_default) || !qparams_ok(pol->q_sensitive) || pol->passthrough_below < 0)
+        return PGQ_ERR_PARAM;
+    int64_t off = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const pgq_tensor_in& x = t[i];
+        pgq_status st = check_tensor_in(x);
+        if (st != PGQ_OK) return st;
+        pgq_tensor_plan& p = plan[i];
+        memset(&p, 0, sizeof(p));
+        p.codes_off = p.scales_off = p.f16_off = p.awq_off = -1;
+        const int64_t numel = x.rows * x.cols;
+        if (numel < pol->passthrough_below) {
+            p.kind = PGQ_KIND_F16;
+            p.f16_off = off;
+            off = align_up(off + numel * 2, 256);
+        } else {
+            const bool sens = name_matches(x.name, pol);
+            p.qp = sens ? pol->q_sensitive : pol->q_default;
+            p.kind = p.qp.bits;
+            p.has_awq = (!sens && x.awq_s) ? 1 : 0;
+            p.codes_off = off;
+            off = align_up(off + numel, 256);
+            p.scales_off = off;
+            off = align_up(off + x.rows * 2, 256);
+            if (p.has_awq) {
+                p.awq_off = off;
+                off = align_up(off + x.cols * 2, 256);
+            }
+        }
+    }
+    *arena_bytes = (size_t)std::max<int64_t>(off, 256);
+    *workspace_bytes = table_bytes((size_t)n);
+    return PGQ_OK;
+}
+
+pgq_status pgq_export_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan* plan,
+                            void* arena, float* const* dq_out, void* workspace, size_t workspace_bytes,
+                            uint32_t flags, uint32_t* dev_status, void* stream)
+{
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (n == 0) return PGQ_OK;
+    if (!t || !plan) return PGQ_ERR_NULL;
+    if (!arena) return PGQ_ERR_NULL;
+    if (!aligned(arena, 256)) return PGQ_ERR_ALIGN;
+    std::vector<Desc> descs((size_t)n);
+    bool awq = false;
+    for (int32_t i = 0; i < n; ++i) {
+        pgq_status st = check_tensor_in(t[i]);
+        if (st != PGQ_OK) return st;
+        st = check_plan_entry(plan[i]);
+        if (st != PGQ_OK) return st;
+        st = export_desc(t[i], plan[i], static_cast<uint8_t*>(arena), descs[i]);
+        if (st != PGQ_OK) return st;
+        if (dq_out && dq_out[i]) {
+            if (!aligned(dq_out[i], 4)) return PGQ_ERR_ALIGN;
+            descs[i].dq = dq_out[i];
+        }
+        awq = awq || descs[i].awq_s != nullptr;
+        set_vec_flag(descs[i]);
+    }
+    return run_grouped(MODE_EXPORT, awq, descs, workspace, workspace_bytes, flags, dev_status, 0, 0, stream);
+}
+
+pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_tensor_plan* plan,
+                               float* const* mean, int32_t k, void* workspace, size_t workspace_bytes,
+                               uint32_t flags, uint32_t* dev_status, void* stream)
+{
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (k < 1 || k > (1 << 24)) return PGQ_ERR_PARAM;     // k must be exact in binary32
+    if (n == 0) return PGQ_OK;
+    if (!snap || !plan || !mean) return PGQ_ERR_NULL;
+    std::vector<Desc> descs((size_t)n);
+    bool awq = false;
+    for (int32_t i = 0; i < n; ++i) {
+        pgq_status st = check_tensor_in(snap[i]);
+        if (st != PGQ_OK) return st;
+        st = check_plan_entry(plan[i]);
+        if (st != PGQ_OK) return st;
+        st = export_desc(snap[i], plan[i], nullptr, descs[i]);
+        if (st != PGQ_OK) return st;
+        if (snap[i].rows > 0 && snap[i].cols > 0) {
+            if (!mean[i]) return PGQ_ERR_NULL;
+            if (!aligned(mean[i], 4)) return PGQ_ERR_ALIGN;
+        }
+        descs[i].mean = mean[i];
+        awq = awq || descs[i].awq_s != nullptr;
+        set_vec_flag(descs[i]);
+    }
+    return run_grouped(MODE_SQWA, awq, descs, workspace, workspace_bytes, flags, dev_status, k, 0, stream);
+}
+
+}  // extern "C"

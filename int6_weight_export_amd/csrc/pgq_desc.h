@@ -1,0 +1,70 @@
+// pgq_desc.h -- descriptors shared by the host layer and the gfx950 kernels of libpgq.
+//
+// A launch processes "tiles": each tile is up to kWaves * rows_per_wave consecutive rows
+// of one tensor.  One wavefront (64 lanes) owns one row at a time.  Grouped calls put a
+// descriptor table (header, one Desc per tensor, then tile_start[n + 1]: the first tile of
+// each tensor, a prefix sum) into the caller's workspace; single-matrix calls pass one
+// Desc by value in the kernel arguments.
+#pragma once
+#include <stdint.h>
+
+namespace pgq {
+
+constexpr int kWaves = 4;                 // wavefronts per workgroup
+constexpr int kBlock = 64 * kWaves;       // threads per workgroup
+constexpr uint64_t kTableMagic = 0x5047515441424c31ull;   // "PGQTABL1"
+
+enum Mode : int32_t { MODE_EXPORT = 0, MODE_SQWA = 1, MODE_FQ = 2, MODE_FQ_BWD = 3 };
+enum : int32_t { IN_F32 = 0, IN_BF16 = 1 };
+enum : int32_t { KIND_F16 = 16 };
+enum : uint32_t { DF_VEC = 1u };          // 16-byte vector path allowed for this tensor
+
+struct alignas(16) Desc {
+    const void* w;            // input rows (fp32 or bf16), row stride ld elements
+    int8_t* codes;            // rows x cols, dense
+    uint16_t* scales;         // rows fp16
+    void* dq;                 // rows x cols dense: fp32 or bf16 (dq_dtype)
+    const float* awq_s;       // cols activation scales (AWQ) or null
+    uint16_t* awq_out;        // cols fp16 multipliers a_j or null
+    uint16_t* f16_out;        // passthrough: rows x cols fp16, dense
+    float* mean;              // SQWA running mean, rows x cols dense
+    const uint16_t* grad;     // STE backward input (bf16, dense)
+    uint16_t* grad_out;       // STE backward output (bf16, dense)
+    uint8_t* mask;            // STE mask bits, rows x ceil(cols/8)
+    int64_t rows, cols, ld;
+    int64_t rank_top;         // the clip is the rank_top-th largest |x| of the row (1 = max)
+    int32_t kind;             // code bits, or KIND_F16
+    int32_t Q;                // 2^(bits-1) - 1
+    int32_t in_dtype;         // IN_F32 / IN_BF16
+    int32_t dq_dtype;         // IN_F32 / IN_BF16
+    uint32_t flags;           // DF_*
+    int32_t pad[3];
+};
+
+struct alignas(64) TableHeader {
+    uint64_t magic;
+    uint64_t checksum;
+    uint32_t n_desc;
+    uint32_t n_tiles;
+    uint32_t pad[10];
+};
+
+struct KArgs {
+    const TableHeader* hdr;   // null for a single-matrix launch
+    const Desc* table;
+    const uint32_t* tile_start;   // n_desc + 1 entries
+    uint64_t checksum;
+    uint32_t* status;
+    uint32_t n_tiles;
+    int32_t rows_per_wave;
+    int32_t sqwa_k;
+    int32_t fq_mode;          // PGQ_FQ_* for MODE_FQ
+    Desc single;
+};
+
+// Host-side launcher implemented next to the kernels.
+// awq: some tensor applies AWQ multipliers; sel: some tensor clips below its maximum.
+int launch(int mode, bool awq, bool sel, const KArgs& ka, uint32_t grid, void* stream);
+int max_resident_blocks(int mode, bool awq, bool sel, int* per_cu, int* n_cu);
+
+}  // namespace pgq

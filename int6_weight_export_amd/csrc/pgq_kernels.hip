@@ -1,0 +1,779 @@
+// pgq_kernels.hip -- gfx950 (CDNA4) kernels of libpgq: per-row symmetric quantization.
+//
+// Design (HBM-streaming, no dense contraction, so no MFMA):
+//   * one 64-lane wavefront owns one row; a row of up to 2048 fp32 / 2048 bf16 values is
+//     loaded once with 16-byte loads (global_load_dwordx4) and stays in VGPRs while its
+//     clip is found, then every output is written once with coalesced stores;
+//   * the clip is a wave-wide max (k = n), an iterated wave max for ranks near the top,
+//     or an LDS-histogram radix select over the 31-bit magnitude patterns (8, 8, 8, 7
+//     bits), exact for any k;
+//   * persistent workgroups of 4 waves stride over tiles of rows, so a whole model (many
+//     tensors of different widths) is one launch;
+//   * longer rows stream through the same code in register-sized pieces, re-reading the
+//     row (L2) for each select pass and for the output pass.
+// Arithmetic follows the definition step by step in IEEE binary32 (correctly rounded
+// divide, round-to-nearest-even, fp32 denormals kept), so the results are bit-exact:
+//   x = w (* a_j), clip = k-th smallest |x|, s = fp16(clip / Q) (1 if 0),
+//   code = clamp(rne(x / s), -Q, Q), dq = code * s (/ a_j),
+//   STE mask = |x / s| <= Q + 1/2, grad_out = mask ? grad : +0,
+//   SQWA mean = mean + (xhat - mean) / k.
+// Sources: "Swiglu gating ... 10min/16MB Track" (PR #2159), Key Explored Modifications
+// (per-row quantization, percentile clipping, fp16 passthrough, STE fake quantization);
+// "SubSixteen v2" card (PR #69), sections Quantization and Other (6 bits, [-31, 31]);
+// "12L ... Int6AWQ MixedBits" (PR #1495), Submission summary and Mixed-bit details;
+// "Discriminative TTT + SLOT-24" card (PR #1414), Novel Contributions (SQWA).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pgq_desc.h"
+#include "../../include/pgq.h"
+
+namespace pgq {
+namespace {
+
+constexpr int kFastRank = 8;     // ranks up to this use the iterated wave max
+
+#define GLB __attribute__((address_space(1)))
+
+// Pointers taken from descriptors are generic; the data all live in global memory, so cast
+// them once per row (uniform, scalar registers) and address lanes with 32-bit offsets.
+template <class T>
+__device__ __forceinline__ GLB T* gp(T* p) { return (GLB T*)p; }
+template <class T>
+__device__ __forceinline__ const GLB T* gp(const T* p) { return (const GLB T*)p; }
+
+// Builtin vector types: 16-, 8-byte loads and stores through address-space-qualified pointers.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t fbits(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
+
+__device__ __forceinline__ uint16_t f2h(float f)
+{
+    _Float16 h = (_Float16)f;                  // v_cvt_f16_f32: round to nearest even, denormals kept
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+__device__ __forceinline__ uint16_t f2bf(float f)
+{
+    __bf16 b = (__bf16)f;                      // gfx950 v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// ---- wave-wide reductions with DPP (quad swaps, row mirrors, row broadcasts), result uniform --
+// Every step pairs groups whose lanes already hold one value, so the same sequence serves max,
+// sum and or.  Disabled rows read 0, the identity of all three.  Call with all 64 lanes active.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op)
+{
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast15 -> rows 1, 3
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast31 -> rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+struct OpSum { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpOr  { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) { return wave_reduce(v, OpMax()); }
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return wave_reduce(v, OpSum()); }
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) { return wave_reduce(v, OpOr()); }
+
+__device__ __forceinline__ void lds_sync_wave()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// ---- element loads: VEC consecutive elements at 32-bit element offset e of a row --------------
+template <int IN, int VEC>
+__device__ __forceinline__ void load_x(const GLB void* row, uint32_t e, float (&x)[VEC])
+{
+    if constexpr (IN == IN_F32) {
+        const GLB float* p = static_cast<const GLB float*>(row) + e;
+        if constexpr (VEC == 4) {
+            const f32x4 v = *reinterpret_cast<const GLB f32x4*>(p);
+            x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+        } else {
+            static_assert(VEC == 1, "fp32 path uses VEC 4 or 1");
+            x[0] = *p;
+        }
+    } else {
+        const GLB uint16_t* p = static_cast<const GLB uint16_t*>(row) + e;
+        if constexpr (VEC == 8) {
+            const u32x4 v = *reinterpret_cast<const GLB u32x4*>(p);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { x[2 * i] = bitsf(w[i] << 16); x[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u); }
+        } else {
+            static_assert(VEC == 1, "bf16 path uses VEC 8 or 1");
+            x[0] = bitsf((uint32_t)*p << 16);
+        }
+    }
+}
+
+// ---- stores / loads of VEC consecutive values --------------------------------------------------
+template <int VEC>
+__device__ __forceinline__ void store_codes(GLB int8_t* p, const float (&r)[VEC])
+{
+    if constexpr (VEC == 1) {
+        *p = (int8_t)(int)r[0];
+    } else {
+        uint32_t w[VEC / 4];
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i)
+            w[i] = ((uint32_t)(int)r[4 * i] & 0xFFu) | (((uint32_t)(int)r[4 * i + 1] & 0xFFu) << 8) |
+                   (((uint32_t)(int)r[4 * i + 2] & 0xFFu) << 16) | (((uint32_t)(int)r[4 * i + 3] & 0xFFu) << 24);
+        if constexpr (VEC == 4) *reinterpret_cast<GLB uint32_t*>(p) = w[0];
+        else *reinterpret_cast<GLB u32x2*>(p) = u32x2{w[0], w[1]};
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_f32(GLB float* p, const float (&v)[VEC])
+{
+    if constexpr (VEC == 1) {
+        *p = v[0];
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i)
+            reinterpret_cast<GLB f32x4*>(p)[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_f32(const GLB float* p, float (&v)[VEC])
+{
+    if constexpr (VEC == 1) {
+        v[0] = *p;
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+            const f32x4 t = reinterpret_cast<const GLB f32x4*>(p)[i];
+            v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+        }
+    }
+}
+
+// 16-bit values (fp16 or bf16 bit patterns) packed two per dword
+template <int VEC>
+__device__ __forceinline__ void store_u16(GLB uint16_t* p, const uint16_t (&h)[VEC])
+{
+    if constexpr (VEC == 1) {
+        *p = h[0];
+    } else {
+        uint32_t w[VEC / 2];
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) w[i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
+        if constexpr (VEC == 4) *reinterpret_cast<GLB u32x2*>(p) = u32x2{w[0], w[1]};
+        else *reinterpret_cast<GLB u32x4*>(p) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_u16(const GLB uint16_t* p, uint16_t (&h)[VEC])
+{
+    if constexpr (VEC == 1) {
+        h[0] = *p;
+    } else {
+        static_assert(VEC == 8, "16-bit vector loads are 8 wide");
+        const u32x4 v = *reinterpret_cast<const GLB u32x4*>(p);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { h[2 * i] = (uint16_t)(w[i] & 0xFFFF); h[2 * i + 1] = (uint16_t)(w[i] >> 16); }
+    }
+}
+
+// ---- the clip: the r-th largest magnitude key of the row (keys = |x| bit patterns) -------------
+// `each(f)` calls f(key, valid) for every element slot this lane owns.
+template <class Each>
+__device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t* hist, int lane)
+{
+    if (r <= kFastRank) {
+        // iterated maximum: strip the largest distinct magnitudes until r elements are covered
+        uint32_t thr = 0x80000000u;           // consider keys < thr
+        uint32_t rem = (uint32_t)r;
+        for (;;) {
+            uint32_t m = 0;
+            each([&](uint32_t k, bool ok) { if (ok && k < thr) m = max(m, k); });
+            m = wave_max(m);
+            if (rem == 1) return m;
+            uint32_t c = 0;
+            each([&](uint32_t k, bool ok) { c += (ok && k == m) ? 1u : 0u; });
+            c = wave_sum(c);
+            if (c >= rem) return m;
+            rem -= c;
+            thr = m;
+        }
+    }
+    // radix select, most significant digit first: bits 30..23, 22..15, 14..7, 6..0, with a
+    // 256-bin histogram per wave in LDS
+    uint32_t prefix = 0, pmask = 0;
+    uint32_t rem = (uint32_t)r;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+        for (int b = lane; b < 256; b += 64) hist[b] = 0;
+        lds_sync_wave();
+        each([&](uint32_t k, bool ok) {
+            if (ok && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xFFu], 1u);
+        });
+        lds_sync_wave();
+        uint32_t h[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) h[b] = hist[4 * lane + b];
+        lds_sync_wave();
+        const uint32_t s = h[0] + h[1] + h[2] + h[3];
+        uint32_t inc = s;                       // sum over lanes >= lane
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = (uint32_t)__shfl_down((int)inc, off, 64);
+            if (lane + off < 64) inc += v;
+        }
+        uint32_t run = inc - s;                 // count of keys in the bins above this lane's bins
+        int found = -1;
+        uint32_t above = 0;
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+            if (found < 0 && run < rem && run + h[b] >= rem) { found = 4 * lane + b; above = run; }
+            run += h[b];
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        const int src = __ffsll((unsigned long long)bal) - 1;
+        const int digit = __shfl(found, src, 64);
+        rem -= (uint32_t)__shfl((int)above, src, 64);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 0xFFu << shift;
+    }
+    return prefix & 0x7FFFFFFFu;
+}
+
+__device__ __forceinline__ float row_scale(float clip, int Q, uint16_t& s16, uint32_t& st)
+{
+    const float s32 = clip / (float)Q;         // correctly rounded binary32 divide
+    uint16_t b = f2h(s32);
+    if ((b & 0x7FFFu) == 0) b = 0x3C00u;       // scale 1 when fp16(clip / Q) is zero
+    if ((b & 0x7FFFu) == 0x7C00u) st |= PGQ_DEV_SCALE_OVF;
+    s16 = b;
+    return h2f(b);
+}
+
+struct RowCtx {
+    float sf;       // fp32 value of the fp16 scale
+    float rinv;     // fl32(1 / sf)
+    float Qf;       // Q
+    float Qc;       // Q + 1: clamp for the reciprocal estimate
+    float L;        // (Q + 1/2) * sf, exact: the STE mask is |x| <= L
+    float kf;       // SQWA snapshot index
+    int k;
+    int fq_mode;
+};
+
+__device__ __forceinline__ void set_scale(RowCtx& rc, float sf)
+{
+    rc.sf = sf;
+    rc.rinv = 1.0f / sf;                                  // correctly rounded
+    rc.L = ((2.0f * rc.Qf + 1.0f) * sf) * 0.5f;           // (2Q+1) * s has <= 19 bits: exact
+}
+
+// code = clamp(rne(x / s), -Q, Q), bit-identical to rounding the correctly rounded quotient:
+// y = x * fl32(1/s) is within 2^-15.9 of x / s whenever |x / s| <= Q + 2 (relative error
+// <= 2^-23), so rint(y) is the nearest integer to x / s unless y lies within 2^-12 of a
+// half-integer.  A fl32 quotient can only equal a half-integer h (|h| < 2^12) when x / s == h
+// (s has 11 significant bits, x 24), so rne(fl32(x / s)) is the exact rounding of x / s.
+// Chunks with any near-tie lane are recomputed with the correctly rounded divide itself.
+template <int VEC>
+__device__ __forceinline__ void quant_chunk(const float (&x)[VEC], const RowCtx& rc, float (&r)[VEC])
+{
+    bool near = false;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        float y = x[v] * rc.rinv;
+        y = __builtin_amdgcn_fmed3f(y, -rc.Qc, rc.Qc);
+        const float q0 = __builtin_rintf(y);
+        near |= fabsf(fabsf(y - q0) - 0.5f) < 0x1p-12f;
+        r[v] = __builtin_amdgcn_fmed3f(q0, -rc.Qf, rc.Qf);
+    }
+    if (__ballot(near)) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const float t = x[v] / rc.sf;
+            r[v] = fminf(fmaxf(__builtin_rintf(t), -rc.Qf), rc.Qf);
+        }
+    }
+}
+
+// Uniform per-row output pointers (global address space).
+struct RowOut {
+    GLB int8_t* codes;
+    GLB void* dq;
+    GLB float* mean;
+    GLB uint8_t* mask;
+    const GLB uint16_t* grad;
+    GLB uint16_t* gout;
+    bool dq_f32;
+};
+
+__device__ __forceinline__ RowOut row_out(const Desc& d, int64_t row)
+{
+    const int64_t o = row * d.cols;
+    RowOut ro;
+    ro.codes = d.codes ? gp(d.codes) + o : nullptr;
+    ro.dq_f32 = d.dq_dtype == IN_F32;
+    ro.dq = d.dq ? (ro.dq_f32 ? (GLB void*)(gp(static_cast<float*>(d.dq)) + o)
+                              : (GLB void*)(gp(static_cast<uint16_t*>(d.dq)) + o))
+                 : nullptr;
+    ro.mean = d.mean ? gp(d.mean) + o : nullptr;
+    ro.mask = d.mask ? gp(d.mask) + row * ((d.cols + 7) >> 3) : nullptr;
+    ro.grad = d.grad ? gp(d.grad) + o : nullptr;
+    ro.gout = d.grad_out ? gp(d.grad_out) + o : nullptr;
+    return ro;
+}
+
+// ---- outputs of one chunk: VEC consecutive elements at element offset c * VEC of the row ------
+template <int MODE, bool AWQ, int VEC>
+__device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t c, const float (&x)[VEC],
+                                          const float (&a)[VEC], bool has_awq, const RowCtx& rc,
+                                          bool valid, int lane)
+{
+    const uint32_t e = c * VEC;
+    float r[VEC];
+    quant_chunk<VEC>(x, rc, r);
+    float dq[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        dq[v] = r[v] * rc.sf;                     // exact (<= 8 + 11 significant bits); +0 for code 0
+        if constexpr (AWQ) {
+            if (has_awq) dq[v] = dq[v] / a[v];
+        }
+    }
+    if constexpr (MODE == MODE_EXPORT) {
+        if (!valid) return;
+        if (ro.codes) store_codes<VEC>(ro.codes + e, r);
+        if (ro.dq) {
+            if (ro.dq_f32) {
+                store_f32<VEC>(static_cast<GLB float*>(ro.dq) + e, dq);
+            } else {
+                uint16_t h[VEC];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) h[v] = f2bf(dq[v]);
+                store_u16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + e, h);
+            }
+        }
+    } else if constexpr (MODE == MODE_SQWA) {
+        if (!valid) return;
+        GLB float* mp = ro.mean + e;
+        if (rc.k == 1) {
+            store_f32<VEC>(mp, dq);
+        } else {
+            float m[VEC];
+            load_f32<VEC>(mp, m);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const float diff = dq[v] - m[v];
+                const float step = diff / rc.kf;
+                m[v] = m[v] + step;
+            }
+            store_f32<VEC>(mp, m);
+        }
+    } else if constexpr (MODE == MODE_FQ) {
+        bool keep[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) keep[v] = fabsf(x[v]) <= rc.L;
+        // mask bits: bit j % 8 of byte j / 8 of the row
+        if (ro.mask) {
+            if constexpr (VEC == 8) {
+                if (valid) {
+                    uint32_t byte = 0;
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) byte |= keep[v] ? (1u << v) : 0u;
+                    ro.mask[c] = (uint8_t)byte;
+                }
+            } else {
+                // element c = 64 * i + lane: the 64 lanes give 8 whole mask bytes
+                const uint64_t bal = __ballot(valid && keep[0]);
+                const uint32_t byte0 = (c - (uint32_t)lane) >> 3;
+                // lane b < 8 writes byte b of the group when that byte holds an element of the row
+                const bool own = __shfl(valid ? 1 : 0, 8 * (lane & 7), 64) != 0;
+                if (lane < 8 && own) ro.mask[byte0 + lane] = (uint8_t)(bal >> (8 * lane));
+            }
+        }
+        if (!valid) return;
+        uint16_t h[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) h[v] = f2bf(dq[v]);
+        if (ro.dq) store_u16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + e, h);
+        if (ro.codes) store_codes<VEC>(ro.codes + e, r);
+        if (rc.fq_mode == PGQ_FQ_FWD_BWD) {
+            uint16_t g[VEC];
+            load_u16<VEC>(ro.grad + e, g);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) g[v] = keep[v] ? g[v] : (uint16_t)0;
+            store_u16<VEC>(ro.gout + e, g);
+        }
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_awq(const GLB float* s_row, GLB uint16_t* a_out, uint32_t c,
+                                         float (&a)[VEC], uint32_t& st)
+{
+    float s[VEC];
+    load_f32<VEC>(s_row + c * VEC, s);
+    uint16_t h[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        if (!(s[v] > 0.0f) || !(s[v] <= 3.402823466e38f)) st |= PGQ_DEV_BAD_AWQ;
+        h[v] = f2h(__builtin_sqrtf(s[v]));       // correctly rounded sqrt, then fp16
+        a[v] = h2f(h[v]);
+    }
+    if (a_out) store_u16<VEC>(a_out + c * VEC, h);
+}
+
+// ---- one integer-kind row --------------------------------------------------------------------
+template <int MODE, bool AWQ, bool SEL, int IN, int VEC>
+__device__ __forceinline__ void row_quant(const Desc& d, int64_t row, int lane, uint32_t* hist, const KArgs& ka,
+                                          uint32_t& st)
+{
+    constexpr int NCH = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);   // register tile in chunks per lane
+    const int nchunk = (int)(d.cols / VEC);
+    const size_t esz = IN == IN_F32 ? 4 : 2;
+    const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
+    const bool has_awq = AWQ && d.awq_s != nullptr;
+    const GLB float* s_row = has_awq ? gp(d.awq_s) : nullptr;
+    GLB uint16_t* a_out = (has_awq && row == 0 && d.awq_out) ? gp(d.awq_out) : nullptr;
+    const RowOut ro = row_out(d, row);
+
+    RowCtx rc;
+    rc.Qf = (float)d.Q;
+    rc.Qc = (float)d.Q + 1.0f;
+    rc.k = ka.sqwa_k;
+    rc.kf = (float)ka.sqwa_k;
+    rc.fq_mode = ka.fq_mode;
+
+    if (nchunk <= 64 * NCH) {
+        // the whole row lives in registers
+        float x[NCH][VEC];
+        float a[AWQ ? NCH : 1][VEC];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            if (64 * i < nchunk) {
+                const uint32_t c = (uint32_t)(lane + 64 * i);
+                if ((int)c < nchunk) {
+                    load_x<IN, VEC>(wrow, c * VEC, x[i]);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) x[i][v] = 0.0f;
+                }
+            }
+        }
+        if constexpr (AWQ) {
+            if (has_awq) {
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    if (64 * i < nchunk) {
+                        const uint32_t c = (uint32_t)(lane + 64 * i);
+                        if ((int)c < nchunk) {
+                            load_awq<VEC>(s_row, a_out, c, a[i], st);
+#pragma unroll
+                            for (int v = 0; v < VEC; ++v) x[i][v] = x[i][v] * a[i][v];
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < VEC; ++v) a[i][v] = 1.0f;
+                        }
+                    }
+                }
+            }
+        }
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+            if (64 * i < nchunk)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[i][v]) & 0x7FFFFFFFu);   // padding is +0
+        mx = wave_max(mx);
+        if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
+        uint32_t ck = mx;
+        if (SEL && d.rank_top > 1) {
+            auto each = [&](auto&& f) {
+#pragma unroll
+                for (int i = 0; i < NCH; ++i)
+                    if (64 * i < nchunk) {
+                        const bool ok = lane + 64 * i < nchunk;
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) f(fbits(x[i][v]) & 0x7FFFFFFFu, ok);
+                    }
+            };
+            ck = kth_largest(each, d.rank_top, hist, lane);
+        }
+        uint16_t s16;
+        set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
+        if (lane == 0 && d.scales) gp(d.scales)[row] = s16;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            if (64 * i < nchunk) {
+                const uint32_t c = (uint32_t)(lane + 64 * i);
+                const float (&ai)[VEC] = a[AWQ ? i : 0];
+                chunk_out<MODE, AWQ, VEC>(ro, c, x[i], ai, has_awq, rc, (int)c < nchunk, lane);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+        // long row: stream it in pieces; every select pass and the output pass re-read it
+        auto load_chunk = [&](uint32_t c, float (&x)[VEC], float (&a)[VEC], GLB uint16_t* aw) {
+            load_x<IN, VEC>(wrow, c * VEC, x);
+            if (has_awq) {
+                load_awq<VEC>(s_row, aw, c, a, st);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) x[v] = x[v] * a[v];
+            } else {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) a[v] = 1.0f;
+            }
+        };
+        uint32_t mx = 0;
+        for (int base = 0; base < nchunk; base += 64) {
+            const uint32_t c = (uint32_t)(base + lane);
+            if ((int)c < nchunk) {
+                float x[VEC], a[VEC];
+                load_chunk(c, x, a, a_out);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[v]) & 0x7FFFFFFFu);
+            }
+        }
+        mx = wave_max(mx);
+        if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
+        uint32_t ck = mx;
+        if (SEL && d.rank_top > 1) {
+            auto each = [&](auto&& f) {
+                for (int base = 0; base < nchunk; base += 64) {
+                    const uint32_t c = (uint32_t)(base + lane);
+                    if ((int)c < nchunk) {
+                        float x[VEC], a[VEC];
+                        load_chunk(c, x, a, nullptr);
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, true);
+                    }
+                }
+            };
+            ck = kth_largest(each, d.rank_top, hist, lane);
+        }
+        uint16_t s16;
+        set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
+        if (lane == 0 && d.scales) gp(d.scales)[row] = s16;
+        for (int base = 0; base < nchunk; base += 64) {
+            const uint32_t c = (uint32_t)(base + lane);
+            const bool ok = (int)c < nchunk;
+            float x[VEC], a[VEC];
+            if (ok) {
+                load_chunk(c, x, a, nullptr);
+            } else {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) { x[v] = 0.0f; a[v] = 1.0f; }
+            }
+            chunk_out<MODE, AWQ, VEC>(ro, c, x, a, has_awq, rc, ok, lane);
+        }
+    }
+}
+
+// ---- fp16 passthrough row (export: fp16 out + optional fp32 decode; SQWA: fp16 round trip) ---
+template <int MODE, int IN, int VEC>
+__device__ __forceinline__ void row_passthrough(const Desc& d, int64_t row, int lane, const KArgs& ka, uint32_t& st)
+{
+    const int nchunk = (int)(d.cols / VEC);
+    const size_t esz = IN == IN_F32 ? 4 : 2;
+    const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
+    const int64_t o = row * d.cols;
+    GLB uint16_t* hrow = d.f16_out ? gp(d.f16_out) + o : nullptr;
+    GLB float* dqrow = d.dq ? gp(static_cast<float*>(d.dq)) + o : nullptr;
+    GLB float* mrow = d.mean ? gp(d.mean) + o : nullptr;
+    const float kf = (float)ka.sqwa_k;
+    for (int base = 0; base < nchunk; base += 64) {
+        const uint32_t c = (uint32_t)(base + lane);
+        if ((int)c >= nchunk) break;
+        const uint32_t e = c * VEC;
+        float x[VEC];
+        load_x<IN, VEC>(wrow, e, x);
+        uint16_t h[VEC];
+        float y[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            h[v] = f2h(x[v]);
+            y[v] = h2f(h[v]);
+            if (!(fabsf(x[v]) <= 3.402823466e38f)) st |= PGQ_DEV_NONFINITE;
+            else if ((h[v] & 0x7FFFu) == 0x7C00u) st |= PGQ_DEV_F16_OVF;
+        }
+        if constexpr (MODE == MODE_EXPORT) {
+            if (hrow) store_u16<VEC>(hrow + e, h);
+            if (dqrow) store_f32<VEC>(dqrow + e, y);
+        } else {
+            GLB float* mp = mrow + e;
+            if (ka.sqwa_k == 1) {
+                store_f32<VEC>(mp, y);
+            } else {
+                float m[VEC];
+                load_f32<VEC>(mp, m);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    const float diff = y[v] - m[v];
+                    const float step = diff / kf;
+                    m[v] = m[v] + step;
+                }
+                store_f32<VEC>(mp, m);
+            }
+        }
+    }
+}
+
+// ---- STE backward only: grad_out = mask ? grad : +0 --------------------------------------------
+template <int VEC>
+__device__ __forceinline__ void row_fq_bwd(const Desc& d, int64_t row, int lane)
+{
+    const int nchunk = (int)(d.cols / VEC);
+    const RowOut ro = row_out(d, row);
+    for (int base = 0; base < nchunk; base += 64) {
+        const uint32_t c = (uint32_t)(base + lane);
+        if ((int)c >= nchunk) break;
+        const uint32_t e = c * VEC;
+        uint16_t g[VEC];
+        load_u16<VEC>(ro.grad + e, g);
+        if constexpr (VEC == 8) {
+            const uint32_t byte = ro.mask[c];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) g[v] = ((byte >> v) & 1u) ? g[v] : (uint16_t)0;
+        } else {
+            const uint32_t byte = ro.mask[c >> 3];
+            g[0] = ((byte >> (c & 7u)) & 1u) ? g[0] : (uint16_t)0;
+        }
+        store_u16<VEC>(ro.gout + e, g);
+    }
+}
+
+template <int MODE, bool AWQ, bool SEL>
+__device__ __forceinline__ void dispatch_row(const Desc& d, int64_t row, int lane, uint32_t* hist, const KArgs& ka,
+                                             uint32_t& st)
+{
+    const bool vec = (d.flags & DF_VEC) != 0;
+    if constexpr (MODE == MODE_FQ_BWD) {
+        if (vec) row_fq_bwd<8>(d, row, lane);
+        else row_fq_bwd<1>(d, row, lane);
+    } else if constexpr (MODE == MODE_FQ) {
+        if (vec) row_quant<MODE_FQ, false, SEL, IN_BF16, 8>(d, row, lane, hist, ka, st);
+        else row_quant<MODE_FQ, false, SEL, IN_BF16, 1>(d, row, lane, hist, ka, st);
+    } else {
+        if (d.kind == KIND_F16) {
+            if (d.in_dtype == IN_F32) {
+                if (vec) row_passthrough<MODE, IN_F32, 4>(d, row, lane, ka, st);
+                else row_passthrough<MODE, IN_F32, 1>(d, row, lane, ka, st);
+            } else {
+                if (vec) row_passthrough<MODE, IN_BF16, 8>(d, row, lane, ka, st);
+                else row_passthrough<MODE, IN_BF16, 1>(d, row, lane, ka, st);
+            }
+        } else if (d.in_dtype == IN_F32) {
+            if (vec) row_quant<MODE, AWQ, SEL, IN_F32, 4>(d, row, lane, hist, ka, st);
+            else row_quant<MODE, AWQ, SEL, IN_F32, 1>(d, row, lane, hist, ka, st);
+        } else {
+            if (vec) row_quant<MODE, AWQ, SEL, IN_BF16, 8>(d, row, lane, hist, ka, st);
+            else row_quant<MODE, AWQ, SEL, IN_BF16, 1>(d, row, lane, hist, ka, st);
+        }
+    }
+}
+
+template <int MODE, bool AWQ, bool SEL>
+__device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, int lane, uint32_t* hist,
+                                        const KArgs& ka, uint32_t& st)
+{
+    for (int j = 0; j < ka.rows_per_wave; ++j) {
+        const int64_t row = row0 + (int64_t)j * kWaves + wave;
+        if (row < d.rows) dispatch_row<MODE, AWQ, SEL>(d, row, lane, hist, ka, st);
+    }
+}
+
+// Grouped launches read the descriptor table through the restrict-qualified pointers (scalar
+// loads); single-matrix launches take the descriptor from the kernel arguments.  AWQ and SEL
+// (clip below the maximum) are separate instantiations so the common absmax kernel stays lean.
+template <int MODE, bool AWQ, bool SEL>
+__global__ void __launch_bounds__(kBlock) pgq_rows_kernel(const TableHeader* __restrict__ hdr,
+                                                         const Desc* __restrict__ table,
+                                                         const uint32_t* __restrict__ tile_start, KArgs ka)
+{
+    __shared__ uint32_t hist_all[kWaves][256];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    uint32_t* hist = hist_all[wave];
+    uint32_t st = 0;
+    if (hdr) {
+        if (hdr->magic != kTableMagic || hdr->checksum != ka.checksum) {
+            if (threadIdx.x == 0 && ka.status) atomicOr(ka.status, PGQ_DEV_STALE_TABLE);
+            return;
+        }
+        // tiles are visited in increasing order, so the owning tensor only moves forward
+        const int64_t rpb = (int64_t)kWaves * ka.rows_per_wave;
+        uint32_t di = 0;
+        for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x) {
+            while (tile >= tile_start[di + 1]) ++di;
+            do_tile<MODE, AWQ, SEL>(table[di], (int64_t)(tile - tile_start[di]) * rpb, wave, lane, hist, ka, st);
+        }
+    } else {
+        const int64_t rpb = (int64_t)kWaves * ka.rows_per_wave;
+        for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x)
+            do_tile<MODE, AWQ, SEL>(ka.single, (int64_t)tile * rpb, wave, lane, hist, ka, st);
+    }
+    st = wave_or(st);
+    if (st && lane == 0 && ka.status) atomicOr(ka.status, st);
+}
+
+template <int MODE, bool AWQ, bool SEL>
+const void* kernel_ptr() { return reinterpret_cast<const void*>(&pgq_rows_kernel<MODE, AWQ, SEL>); }
+
+template <int MODE>
+const void* pick_mode(bool awq, bool sel)
+{
+    if (awq) return sel ? kernel_ptr<MODE, true, true>() : kernel_ptr<MODE, true, false>();
+    return sel ? kernel_ptr<MODE, false, true>() : kernel_ptr<MODE, false, false>();
+}
+
+const void* pick(int mode, bool awq, bool sel)
+{
+    switch (mode) {
+    case MODE_EXPORT: return pick_mode<MODE_EXPORT>(awq, sel);
+    case MODE_SQWA: return pick_mode<MODE_SQWA>(awq, sel);
+    case MODE_FQ: return sel ? kernel_ptr<MODE_FQ, false, true>() : kernel_ptr<MODE_FQ, false, false>();
+    case MODE_FQ_BWD: return kernel_ptr<MODE_FQ_BWD, false, false>();
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+int launch(int mode, bool awq, bool sel, const KArgs& ka, uint32_t grid, void* stream)
+{
+    const void* fn = pick(mode, awq, sel);
+    if (!fn || grid == 0) return (int)hipErrorInvalidValue;
+    KArgs copy = ka;
+    const TableHeader* hdr = ka.hdr;
+    const Desc* table = ka.table;
+    const uint32_t* tile_start = ka.tile_start;
+    void* args[] = {&hdr, &table, &tile_start, &copy};
+    return (int)hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
+}
+
+int max_resident_blocks(int mode, bool awq, bool sel, int* per_cu, int* n_cu)
+{
+    const void* fn = pick(mode, awq, sel);
+    if (!fn) return (int)hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return (int)e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fn, kBlock, 0);
+    return (int)e;
+}
+
+}  // namespace pgq

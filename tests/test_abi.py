@@ -1,0 +1,177 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/pgq.h
+declares, rejects bad arguments synchronously, and plans exports like the oracle's policy.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pgq.h")
+
+pgq = pytest.importorskip("int6_weight_export_amd.pgq")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(pgq_[a-z_0-9]+)\s*\(", txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 8, names
+    lib = ctypes.CDLL(pgq.LIB_PATH)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+        assert nm in pgq.SIGNATURES, nm
+    assert set(pgq.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in pgq.pgq_version()
+    for s in range(8):
+        assert pgq.pgq_status_str(s)
+
+
+FAKE = 0x10000      # a non-null, aligned address never dereferenced (validation fails or no launch)
+
+
+def q(bits=6, num=1, den=1):
+    return pgq.pgq_qparams(bits, num, den)
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(rows=-1), pgq.PGQ_ERR_SHAPE),
+    (dict(ld=100, cols=200), pgq.PGQ_ERR_SHAPE),
+    (dict(cols=0), pgq.PGQ_ERR_SHAPE),
+    (dict(qp=q(9)), pgq.PGQ_ERR_PARAM),
+    (dict(qp=q(1)), pgq.PGQ_ERR_PARAM),
+    (dict(qp=q(6, 1, 0)), pgq.PGQ_ERR_PARAM),
+    (dict(qp=q(6, 3, 2)), pgq.PGQ_ERR_PARAM),
+    (dict(w_dtype=5), pgq.PGQ_ERR_DTYPE),
+    (dict(dq=FAKE, dq_dtype=9), pgq.PGQ_ERR_DTYPE),
+    (dict(scales=None), pgq.PGQ_ERR_NULL),
+    (dict(w=None), pgq.PGQ_ERR_NULL),
+    (dict(awq_mult=FAKE), pgq.PGQ_ERR_NULL),
+    (dict(w=FAKE + 2), pgq.PGQ_ERR_ALIGN),
+    (dict(scales=FAKE + 1), pgq.PGQ_ERR_ALIGN),
+])
+def test_quantize_rows_argument_errors(args, want):
+    a = dict(w=FAKE, w_dtype=pgq.PGQ_F32, rows=4, cols=200, ld=200, qp=q(), awq_s=None, awq_mult=None,
+             codes=FAKE, scales=FAKE, dq=None, dq_dtype=pgq.PGQ_F32, dev_status=None, stream=None)
+    a.update(args)
+    if "ld" not in args:
+        a["ld"] = a["cols"]
+    assert pgq.pgq_quantize_rows(**a) == want
+
+
+def test_fakequant_argument_errors():
+    t = (pgq.pgq_fq_tensor * 1)()
+    t[0] = pgq.pgq_fq_tensor(FAKE, 4, 16, 16, FAKE, FAKE, FAKE, 0, 0, 0)
+    assert pgq.pgq_fakequant_fwd_bwd(0, t, 1, q(), None, 0, 0, None, None) == pgq.PGQ_ERR_PARAM
+    assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD, t, -1, q(), None, 0, 0, None, None) == pgq.PGQ_ERR_SHAPE
+    assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_BWD, t, 1, q(), None, 0, 0, None, None) == pgq.PGQ_ERR_NULL
+    assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD_BWD, t, 1, q(), None, 0, 0, None, None) == pgq.PGQ_ERR_NULL
+    t[0].dq = 0
+    assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD, t, 1, q(), None, 0, 0, None, None) == pgq.PGQ_ERR_NULL
+    t[0].dq = FAKE
+    t2 = (pgq.pgq_fq_tensor * 2)(t[0], t[0])
+    assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD, t2, 2, q(), None, 0, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
+    need = ctypes.c_size_t(0)
+    assert pgq.pgq_fakequant_workspace(t2, 2, ctypes.byref(need)) == pgq.PGQ_OK and need.value > 0
+    assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD, t2, 2, q(), FAKE, need.value - 8, 0, None,
+                                     None) == pgq.PGQ_ERR_WORKSPACE
+
+
+def _tensor_array(ts, awq=False):
+    arr = (pgq.pgq_tensor_in * len(ts))()
+    keep = []
+    for i, t in enumerate(ts):
+        rows, cols = oracle.as_rows(t.shape)
+        nm = t.name.encode()
+        keep.append(nm)
+        arr[i] = pgq.pgq_tensor_in(nm, FAKE, pgq.PGQ_F32, 0, rows, cols, cols,
+                                   FAKE if (awq and t.awq_s is not None) else 0)
+    return arr, keep
+
+
+def _policy(patterns=oracle.DEFAULT_INT8_PATTERNS, below=65536, q6=(6, 9999, 10000), q8=(8, 1, 1)):
+    pats = [p.encode() for p in patterns]
+    parr = (ctypes.c_char_p * max(1, len(pats)))(*pats)
+    pol = pgq.pgq_policy(ctypes.cast(parr, ctypes.POINTER(ctypes.c_char_p)), len(pats), 0, below,
+                         pgq.pgq_qparams(*q6), pgq.pgq_qparams(*q8))
+    return pol, (pats, parr)
+
+
+@pytest.mark.parametrize("cfg", ["gpt9", "gpt12", "gpt9_all_int6"])
+def test_export_plan_matches_oracle_policy(cfg):
+    if cfg == "gpt12":
+        ts = synth.config4()
+        pol, keep = _policy(q6=(6, 1, 1))
+        opol = oracle.Policy(q6=(6, 1, 1))
+    elif cfg == "gpt9":
+        ts = synth.config2()
+        pol, keep = _policy()
+        opol = oracle.Policy()
+    else:
+        ts = synth.config2()
+        pol, keep = _policy(patterns=())
+        opol = oracle.Policy(int8_patterns=())
+    arr, k2 = _tensor_array(ts, awq=True)
+    plan = (pgq.pgq_tensor_plan * len(ts))()
+    ab, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert pgq.pgq_export_plan(arr, len(ts), ctypes.byref(pol), plan, ctypes.byref(ab), ctypes.byref(wb)) == 0
+    regions = []
+    for i, t in enumerate(ts):
+        kind = oracle.tensor_kind(t.name, t.numel, opol)
+        p = plan[i]
+        assert p.kind == kind, t.name
+        rows, cols = oracle.as_rows(t.shape)
+        if kind == oracle.KIND_F16:
+            regions.append((p.f16_off, 2 * t.numel))
+            assert p.codes_off == -1 and p.scales_off == -1
+        else:
+            want_q = opol.q8 if kind == oracle.KIND_INT8 else opol.q6
+            assert (p.qp.bits, p.qp.pct_num, p.qp.pct_den) == want_q
+            regions += [(p.codes_off, rows * cols), (p.scales_off, 2 * rows)]
+            assert p.has_awq == int(t.awq_s is not None and kind == oracle.KIND_INT6)
+            if p.has_awq:
+                regions.append((p.awq_off, 2 * cols))
+    # regions are 256-byte aligned, disjoint and inside the arena
+    regions.sort()
+    for (o1, n1), (o2, n2) in zip(regions, regions[1:]):
+        assert o1 % 256 == 0 and o1 + n1 <= o2
+    assert regions[-1][0] + regions[-1][1] <= ab.value
+    assert wb.value > 0
+
+
+def test_export_and_sqwa_argument_errors():
+    ts = synth.config2()[:3]
+    arr, keep = _tensor_array(ts)
+    pol, k2 = _policy()
+    plan = (pgq.pgq_tensor_plan * 3)()
+    ab, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert pgq.pgq_export_plan(arr, 3, ctypes.byref(pol), plan, ctypes.byref(ab), ctypes.byref(wb)) == 0
+    assert pgq.pgq_export_plan(arr, 3, None, plan, ctypes.byref(ab), ctypes.byref(wb)) == pgq.PGQ_ERR_NULL
+    bad, k3 = _policy(q6=(6, 2, 1))
+    assert pgq.pgq_export_plan(arr, 3, ctypes.byref(bad), plan, ctypes.byref(ab),
+                               ctypes.byref(wb)) == pgq.PGQ_ERR_PARAM
+    assert pgq.pgq_export_model(arr, 3, plan, None, None, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_NULL
+    assert pgq.pgq_export_model(arr, 3, plan, FAKE + 64, None, FAKE, wb.value, 0, None,
+                                None) == pgq.PGQ_ERR_ALIGN
+    assert pgq.pgq_export_model(arr, 3, plan, FAKE, None, FAKE, wb.value - 8, 0, None,
+                                None) == pgq.PGQ_ERR_WORKSPACE
+    assert pgq.pgq_export_model(arr, 3, plan, FAKE, None, None, 0, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
+    plan[0].kind = 5  # bits 5 without matching qparams
+    assert pgq.pgq_export_model(arr, 3, plan, FAKE, None, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM
+    means = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    assert pgq.pgq_sqwa_accumulate(arr, 3, plan, means, 0, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM
+    arr[1].dtype = 4
+    assert pgq.pgq_export_plan(arr, 3, ctypes.byref(pol), plan, ctypes.byref(ab),
+                               ctypes.byref(wb)) == pgq.PGQ_ERR_DTYPE
