@@ -30,10 +30,17 @@ int env_int(const char* name, int dflt, int lo, int hi)
     return std::min(std::max(x, lo), hi);
 }
 
-// Rows per wavefront in one tile (a tile is kWaves * rows_per_wave rows of one tensor).
-int rows_per_wave()
+// Row groups per wavefront in one tile (a tile is kWaves * rgroup * groups rows of a tensor).
+int groups_per_wave()
 {
-    static const int v = env_int("PGQ_ROWS_PER_WAVE", 2, 1, 64);
+    static const int v = env_int("PGQ_GROUPS_PER_WAVE", 1, 1, 64);
+    return v;
+}
+
+// Upper bound on the rows a wavefront processes together.
+int max_rgroup()
+{
+    static const int v = env_int("PGQ_MAX_RGROUP", 8, 1, 8);
     return v;
 }
 
@@ -105,23 +112,40 @@ void set_vec_flag(Desc& d)
     d.flags = ok ? DF_VEC : 0u;
 }
 
+// Kernel features a tensor needs (see F_* in pgq_desc.h).
+uint32_t features_of(const Desc& d)
+{
+    if (d.rows <= 0 || d.cols <= 0) return 0;
+    uint32_t f = d.in_dtype == IN_F32 ? F_F32 : F_BF16;
+    const bool vec = (d.flags & DF_VEC) != 0;
+    if (!vec) f |= F_SCALAR;
+    if (d.kind == KIND_F16) return f | F_PASS;
+    if (d.awq_s) f |= F_AWQ;
+    if (d.rank_top > 1) f |= F_SEL;
+    const int64_t reg_cols = !vec ? kRegCols_Scalar : (d.in_dtype == IN_F32 ? kRegCols_F32 : kRegCols_BF16);
+    if (d.cols > reg_cols) f |= F_LONG;
+    return f;
+}
+
 Desc blank_desc()
 {
     Desc d;
     memset(&d, 0, sizeof(d));
     d.rank_top = 1;
+    d.rgroup = 1;
+    d.tile_rows = kWaves;
     return d;
 }
 
 struct LimitCache {
     std::mutex mu;
-    // [device][mode*4+awq*2+sel] -> resident blocks per CU; n_cu per device
+    // [device][mode][variant] -> resident blocks per CU; n_cu per device
     std::vector<std::vector<int>> per_cu;
     std::vector<int> n_cu;
 };
 LimitCache g_limits;
 
-uint32_t grid_for(int mode, bool awq, bool sel, uint32_t n_tiles)
+uint32_t grid_for(int mode, uint32_t need, uint32_t n_tiles)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -129,13 +153,13 @@ uint32_t grid_for(int mode, bool awq, bool sel, uint32_t n_tiles)
     {
         std::lock_guard<std::mutex> lk(g_limits.mu);
         if ((int)g_limits.per_cu.size() <= dev) {
-            g_limits.per_cu.resize(dev + 1, std::vector<int>(16, -1));
+            g_limits.per_cu.resize(dev + 1, std::vector<int>(4 * 128, -1));
             g_limits.n_cu.resize(dev + 1, -1);
         }
-        int& slot = g_limits.per_cu[dev][mode * 4 + (awq ? 2 : 0) + (sel ? 1 : 0)];
+        int& slot = g_limits.per_cu[dev][mode * 128 + variant_of(mode, need)];
         if (slot < 0 || g_limits.n_cu[dev] < 0) {
             int pc = 0, nc = 0;
-            if (max_resident_blocks(mode, awq, sel, &pc, &nc) != 0 || pc <= 0 || nc <= 0) { pc = 4; nc = 256; }
+            if (max_resident_blocks(mode, need, &pc, &nc) != 0 || pc <= 0 || nc <= 0) { pc = 4; nc = 256; }
             slot = pc;
             g_limits.n_cu[dev] = nc;
         }
@@ -154,14 +178,36 @@ size_t table_bytes(size_t n_desc)
            (size_t)align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 8);
 }
 
-uint64_t tiles_for(int64_t rows)
+// Rows a wavefront loads together: as many as the register tile holds (a power of two).
+void set_grouping(Desc& d, int mode)
 {
-    const int64_t rpb = (int64_t)kWaves * rows_per_wave();
-    return rows > 0 ? (uint64_t)((rows + rpb - 1) / rpb) : 0;
+    int R = 1;
+    if (mode != MODE_FQ_BWD && d.kind != KIND_F16 && d.cols > 0) {
+        const bool vec = (d.flags & DF_VEC) != 0;
+        const int64_t nchunk = vec ? d.cols / (d.in_dtype == IN_F32 ? 4 : 8) : d.cols;
+        const int ncht = vec ? (d.in_dtype == IN_F32 ? 8 : 4) : 16;
+        const int64_t nch = (nchunk + 63) / 64;
+        if (nch <= ncht) {
+            int p2 = 1;
+            while (p2 < nch) p2 <<= 1;
+            R = std::min(std::min(ncht / p2, 8), max_rgroup());
+            int r2 = 1;
+            while (r2 * 2 <= R) r2 *= 2;
+            R = r2;
+        }
+    }
+    d.rgroup = R;
+    d.tile_rows = kWaves * R * groups_per_wave();
+}
+
+uint64_t tiles_for(const Desc& d)
+{
+    if (d.rows <= 0 || d.cols <= 0) return 0;
+    return (uint64_t)((d.rows + d.tile_rows - 1) / d.tile_rows);
 }
 
 // Build the table on the host, upload it (unless resident) and launch one grouped kernel.
-pgq_status run_grouped(int mode, bool awq, const std::vector<Desc>& descs, void* ws, size_t ws_bytes,
+pgq_status run_grouped(int mode, const std::vector<Desc>& descs, void* ws, size_t ws_bytes,
                        uint32_t flags, uint32_t* dev_status, int sqwa_k, int fq_mode, void* stream)
 {
     const size_t n = descs.size();
@@ -169,7 +215,7 @@ pgq_status run_grouped(int mode, bool awq, const std::vector<Desc>& descs, void*
     uint64_t total = 0;
     for (size_t i = 0; i < n; ++i) {
         start[i] = (uint32_t)total;
-        if (descs[i].cols > 0) total += tiles_for(descs[i].rows);
+        total += tiles_for(descs[i]);
         if (total > 0xFFFFFFF0ull) return PGQ_ERR_SHAPE;
     }
     start[n] = (uint32_t)total;
@@ -187,7 +233,7 @@ pgq_status run_grouped(int mode, bool awq, const std::vector<Desc>& descs, void*
     memcpy(buf + desc_off, descs.data(), n * sizeof(Desc));
     memcpy(buf + start_off, start.data(), (n + 1) * sizeof(uint32_t));
     uint64_t h = table_hash(buf + desc_off, need - desc_off, 0x243F6A8885A308D3ull ^ (uint64_t)mode);
-    h = table_hash(&total, 8, h ^ (uint64_t)rows_per_wave());
+    h = table_hash(&total, 8, h);
     hdr->magic = kTableMagic;
     hdr->checksum = h;
     hdr->n_desc = (uint32_t)n;
@@ -206,35 +252,32 @@ pgq_status run_grouped(int mode, bool awq, const std::vector<Desc>& descs, void*
     ka.checksum = h;
     ka.status = dev_status;
     ka.n_tiles = (uint32_t)total;
-    ka.rows_per_wave = rows_per_wave();
     ka.sqwa_k = sqwa_k;
     ka.fq_mode = fq_mode;
     ka.single = blank_desc();
-    bool sel = false;
-    for (const Desc& d : descs) sel = sel || (d.rank_top > 1 && d.kind != KIND_F16);
-    const uint32_t grid = grid_for(mode, awq, sel, ka.n_tiles);
-    if (launch(mode, awq, sel, ka, grid, stream) != 0) return PGQ_ERR_HIP;
+    uint32_t feats = 0;
+    for (const Desc& d : descs) feats |= features_of(d);
+    const uint32_t grid = grid_for(mode, feats, ka.n_tiles);
+    if (launch(mode, feats, ka, grid, stream) != 0) return PGQ_ERR_HIP;
     if (hipGetLastError() != hipSuccess) return PGQ_ERR_HIP;
     return PGQ_OK;
 }
 
-pgq_status run_single(int mode, bool awq, const Desc& d, uint32_t* dev_status, int sqwa_k, int fq_mode,
-                      void* stream)
+pgq_status run_single(int mode, const Desc& d, uint32_t* dev_status, int sqwa_k, int fq_mode, void* stream)
 {
     if (d.rows <= 0 || d.cols <= 0) return PGQ_OK;
     KArgs ka;
     memset(&ka, 0, sizeof(ka));
     ka.status = dev_status;
-    ka.rows_per_wave = rows_per_wave();
-    const uint64_t nt = tiles_for(d.rows);
+    const uint64_t nt = tiles_for(d);
     if (nt > 0xFFFFFFFFull) return PGQ_ERR_SHAPE;
     ka.n_tiles = (uint32_t)nt;
     ka.sqwa_k = sqwa_k;
     ka.fq_mode = fq_mode;
     ka.single = d;
-    const bool sel = d.rank_top > 1;
-    const uint32_t grid = grid_for(mode, awq, sel, ka.n_tiles);
-    if (launch(mode, awq, sel, ka, grid, stream) != 0) return PGQ_ERR_HIP;
+    const uint32_t need = features_of(d);
+    const uint32_t grid = grid_for(mode, need, ka.n_tiles);
+    if (launch(mode, need, ka, grid, stream) != 0) return PGQ_ERR_HIP;
     if (hipGetLastError() != hipSuccess) return PGQ_ERR_HIP;
     return PGQ_OK;
 }
@@ -357,7 +400,8 @@ pgq_status pgq_quantize_rows(const void* w, int32_t w_dtype, int64_t rows, int64
     d.in_dtype = w_dtype == PGQ_F32 ? IN_F32 : IN_BF16;
     d.dq_dtype = dq_dtype == PGQ_F32 ? IN_F32 : IN_BF16;
     set_vec_flag(d);
-    return run_single(MODE_EXPORT, awq_s != nullptr, d, dev_status, 0, 0, stream);
+    set_grouping(d, MODE_EXPORT);
+    return run_single(MODE_EXPORT, d, dev_status, 0, 0, stream);
 }
 
 pgq_status pgq_fakequant_workspace(const pgq_fq_tensor* t, int32_t n, size_t* workspace_bytes)
@@ -423,10 +467,11 @@ pgq_status pgq_fakequant_fwd_bwd(int32_t mode, const pgq_fq_tensor* t, int32_t n
             const bool ok = d.cols % 8 == 0 && aligned(d.grad, 16) && aligned(d.grad_out, 16);
             d.flags = ok ? DF_VEC : 0u;
         }
+        set_grouping(d, fwd ? MODE_FQ : MODE_FQ_BWD);
     }
     const int kmode = fwd ? MODE_FQ : MODE_FQ_BWD;
-    if (n == 1 && !workspace) return run_single(kmode, false, descs[0], dev_status, 0, mode, stream);
-    return run_grouped(kmode, false, descs, workspace, workspace_bytes, flags, dev_status, 0, mode, stream);
+    if (n == 1 && !workspace) return run_single(kmode, descs[0], dev_status, 0, mode, stream);
+    return run_grouped(kmode, descs, workspace, workspace_bytes, flags, dev_status, 0, mode, stream);
 }
 
 pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* pol,
@@ -480,7 +525,6 @@ pgq_status pgq_export_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_
     if (!arena) return PGQ_ERR_NULL;
     if (!aligned(arena, 256)) return PGQ_ERR_ALIGN;
     std::vector<Desc> descs((size_t)n);
-    bool awq = false;
     for (int32_t i = 0; i < n; ++i) {
         pgq_status st = check_tensor_in(t[i]);
         if (st != PGQ_OK) return st;
@@ -492,10 +536,10 @@ pgq_status pgq_export_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_
             if (!aligned(dq_out[i], 4)) return PGQ_ERR_ALIGN;
             descs[i].dq = dq_out[i];
         }
-        awq = awq || descs[i].awq_s != nullptr;
         set_vec_flag(descs[i]);
+        set_grouping(descs[i], MODE_EXPORT);
     }
-    return run_grouped(MODE_EXPORT, awq, descs, workspace, workspace_bytes, flags, dev_status, 0, 0, stream);
+    return run_grouped(MODE_EXPORT, descs, workspace, workspace_bytes, flags, dev_status, 0, 0, stream);
 }
 
 pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_tensor_plan* plan,
@@ -507,7 +551,6 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
     if (n == 0) return PGQ_OK;
     if (!snap || !plan || !mean) return PGQ_ERR_NULL;
     std::vector<Desc> descs((size_t)n);
-    bool awq = false;
     for (int32_t i = 0; i < n; ++i) {
         pgq_status st = check_tensor_in(snap[i]);
         if (st != PGQ_OK) return st;
@@ -520,10 +563,10 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
             if (!aligned(mean[i], 4)) return PGQ_ERR_ALIGN;
         }
         descs[i].mean = mean[i];
-        awq = awq || descs[i].awq_s != nullptr;
         set_vec_flag(descs[i]);
+        set_grouping(descs[i], MODE_SQWA);
     }
-    return run_grouped(MODE_SQWA, awq, descs, workspace, workspace_bytes, flags, dev_status, k, 0, stream);
+    return run_grouped(MODE_SQWA, descs, workspace, workspace_bytes, flags, dev_status, k, 0, stream);
 }
 
 }  // extern "C"

@@ -19,6 +19,20 @@ enum : int32_t { IN_F32 = 0, IN_BF16 = 1 };
 enum : int32_t { KIND_F16 = 16 };
 enum : uint32_t { DF_VEC = 1u };          // 16-byte vector path allowed for this tensor
 
+// Features a launch needs; each kernel instantiation covers a fixed set of them, and the
+// host launches the leanest one that covers what its tensors need (fewer paths compiled
+// in means fewer registers and higher occupancy).
+enum : uint32_t {
+    F_F32 = 1u,       // fp32 inputs
+    F_BF16 = 2u,      // bf16 inputs
+    F_PASS = 4u,      // fp16 passthrough tensors
+    F_AWQ = 8u,       // AWQ column multipliers
+    F_SEL = 16u,      // clip below the row maximum (percentile select)
+    F_SCALAR = 32u,   // unaligned tensors (element-wise path)
+    F_LONG = 64u,     // rows longer than the register tile
+    F_ALL = 127u
+};
+
 struct alignas(16) Desc {
     const void* w;            // input rows (fp32 or bf16), row stride ld elements
     int8_t* codes;            // rows x cols, dense
@@ -38,7 +52,9 @@ struct alignas(16) Desc {
     int32_t in_dtype;         // IN_F32 / IN_BF16
     int32_t dq_dtype;         // IN_F32 / IN_BF16
     uint32_t flags;           // DF_*
-    int32_t pad[3];
+    int32_t rgroup;           // rows a wave processes together (1, 2, 4 or 8)
+    int32_t tile_rows;        // rows per tile: kWaves * rgroup * groups per wave
+    int32_t pad;
 };
 
 struct alignas(64) TableHeader {
@@ -56,15 +72,22 @@ struct KArgs {
     uint64_t checksum;
     uint32_t* status;
     uint32_t n_tiles;
-    int32_t rows_per_wave;
+    int32_t reserved;
     int32_t sqwa_k;
     int32_t fq_mode;          // PGQ_FQ_* for MODE_FQ
     Desc single;
 };
 
 // Host-side launcher implemented next to the kernels.
-// awq: some tensor applies AWQ multipliers; sel: some tensor clips below its maximum.
-int launch(int mode, bool awq, bool sel, const KArgs& ka, uint32_t grid, void* stream);
-int max_resident_blocks(int mode, bool awq, bool sel, int* per_cu, int* n_cu);
+// need: the F_* features of the launch.  variant_of() names the instantiation used (its
+// feature set); launch() and max_resident_blocks() take the same `need`.
+uint32_t variant_of(int mode, uint32_t need);
+int launch(int mode, uint32_t need, const KArgs& ka, uint32_t grid, void* stream);
+int max_resident_blocks(int mode, uint32_t need, int* per_cu, int* n_cu);
+
+// Register tile: a row of up to 64 * chunks * elements stays in VGPRs; longer rows stream.
+constexpr int64_t kRegCols_F32 = 64 * 8 * 4;     // 2048
+constexpr int64_t kRegCols_BF16 = 64 * 4 * 8;    // 2048
+constexpr int64_t kRegCols_Scalar = 64 * 16;     // 1024
 
 }  // namespace pgq

@@ -198,8 +198,10 @@ __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t
         // iterated maximum: strip the largest distinct magnitudes until r elements are covered
         uint32_t thr = 0x80000000u;           // consider keys < thr
         uint32_t rem = (uint32_t)r;
-        for (;;) {
-            uint32_t m = 0;
+        uint32_t m = 0;
+        // each round removes at least one element, so r rounds always suffice
+        for (int round = 0; round < kFastRank; ++round) {
+            m = 0;
             each([&](uint32_t k, bool ok) { if (ok && k < thr) m = max(m, k); });
             m = wave_max(m);
             if (rem == 1) return m;
@@ -210,6 +212,7 @@ __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t
             rem -= c;
             thr = m;
         }
+        return m;
     }
     // radix select, most significant digit first: bits 30..23, 22..15, 14..7, 6..0, with a
     // 256-bin histogram per wave in LDS
@@ -244,7 +247,7 @@ __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t
             run += h[b];
         }
         const uint64_t bal = __ballot(found >= 0);
-        const int src = __ffsll((unsigned long long)bal) - 1;
+        const int src = bal ? __ffsll((unsigned long long)bal) - 1 : 0;
         const int digit = __shfl(found, src, 64);
         rem -= (uint32_t)__shfl((int)above, src, 64);
         prefix |= (uint32_t)digit << shift;
@@ -287,6 +290,8 @@ __device__ __forceinline__ void set_scale(RowCtx& rc, float sf)
 // half-integer.  A fl32 quotient can only equal a half-integer h (|h| < 2^12) when x / s == h
 // (s has 11 significant bits, x 24), so rne(fl32(x / s)) is the exact rounding of x / s.
 // Chunks with any near-tie lane are recomputed with the correctly rounded divide itself.
+// Codes are integers held in floats; zero is kept as +0 so that code * s is +0, as it is for
+// an integer code converted back to binary32.
 template <int VEC>
 __device__ __forceinline__ void quant_chunk(const float (&x)[VEC], const RowCtx& rc, float (&r)[VEC])
 {
@@ -297,13 +302,13 @@ __device__ __forceinline__ void quant_chunk(const float (&x)[VEC], const RowCtx&
         y = __builtin_amdgcn_fmed3f(y, -rc.Qc, rc.Qc);
         const float q0 = __builtin_rintf(y);
         near |= fabsf(fabsf(y - q0) - 0.5f) < 0x1p-12f;
-        r[v] = __builtin_amdgcn_fmed3f(q0, -rc.Qf, rc.Qf);
+        r[v] = __builtin_amdgcn_fmed3f(q0, -rc.Qf, rc.Qf) + 0.0f;   // + 0 turns a -0 code into +0
     }
     if (__ballot(near)) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
             const float t = x[v] / rc.sf;
-            r[v] = fminf(fmaxf(__builtin_rintf(t), -rc.Qf), rc.Qf);
+            r[v] = fminf(fmaxf(__builtin_rintf(t), -rc.Qf), rc.Qf) + 0.0f;
         }
     }
 }
@@ -435,19 +440,24 @@ __device__ __forceinline__ void load_awq(const GLB float* s_row, GLB uint16_t* a
     if (a_out) store_u16<VEC>(a_out + c * VEC, h);
 }
 
-// ---- one integer-kind row --------------------------------------------------------------------
-template <int MODE, bool AWQ, bool SEL, int IN, int VEC>
-__device__ __forceinline__ void row_quant(const Desc& d, int64_t row, int lane, uint32_t* hist, const KArgs& ka,
-                                          uint32_t& st)
+// ---- a group of R consecutive rows of one tensor (integer kinds) ------------------------------
+// The register tile holds NCHT chunks per lane.  A row needing NCHT / R chunks or fewer is
+// processed R rows at a time: every row's loads are issued before the first reduction, so a
+// wave keeps R rows in flight.  Rows longer than the tile (R = 1 only) stream in pieces.
+template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R>
+__device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
+                                           const KArgs& ka, uint32_t& st)
 {
-    constexpr int NCH = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);   // register tile in chunks per lane
+    constexpr int NCHT = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);   // register tile, chunks per lane
+    constexpr int NCH = NCHT / R;                                       // chunks per lane per row
+    static_assert(NCH * R == NCHT, "R divides the register tile");
+    static_assert(64 * NCHT * VEC == (VEC == 1 ? kRegCols_Scalar : (IN == IN_F32 ? kRegCols_F32 : kRegCols_BF16)),
+                  "register tile must match the host's long-row threshold");
     const int nchunk = (int)(d.cols / VEC);
     const size_t esz = IN == IN_F32 ? 4 : 2;
-    const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
     const bool has_awq = AWQ && d.awq_s != nullptr;
     const GLB float* s_row = has_awq ? gp(d.awq_s) : nullptr;
-    GLB uint16_t* a_out = (has_awq && row == 0 && d.awq_out) ? gp(d.awq_out) : nullptr;
-    const RowOut ro = row_out(d, row);
+    GLB uint16_t* a_out = (has_awq && row0 == 0 && d.awq_out) ? gp(d.awq_out) : nullptr;
 
     RowCtx rc;
     rc.Qf = (float)d.Q;
@@ -456,75 +466,95 @@ __device__ __forceinline__ void row_quant(const Desc& d, int64_t row, int lane, 
     rc.kf = (float)ka.sqwa_k;
     rc.fq_mode = ka.fq_mode;
 
-    if (nchunk <= 64 * NCH) {
-        // the whole row lives in registers
-        float x[NCH][VEC];
+    if (R > 1 || !LONG || nchunk <= 64 * NCH) {
+        float x[R][NCH][VEC];
         float a[AWQ ? NCH : 1][VEC];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            if (64 * i < nchunk) {
-                const uint32_t c = (uint32_t)(lane + 64 * i);
-                if ((int)c < nchunk) {
-                    load_x<IN, VEC>(wrow, c * VEC, x[i]);
-                } else {
+        for (int r = 0; r < R; ++r) {
+            if (r < nrows) {
+                const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)((row0 + r) * d.ld) * esz;
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) x[i][v] = 0.0f;
+                for (int i = 0; i < NCH; ++i) {
+                    if (64 * i < nchunk) {
+                        const uint32_t c = (uint32_t)(lane + 64 * i);
+                        if ((int)c < nchunk) {
+                            load_x<IN, VEC>(wrow, c * VEC, x[r][i]);
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < VEC; ++v) x[r][i][v] = 0.0f;
+                        }
+                    }
                 }
             }
         }
         if constexpr (AWQ) {
             if (has_awq) {
+                // the column multipliers are the same for every row of the group
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
                     if (64 * i < nchunk) {
                         const uint32_t c = (uint32_t)(lane + 64 * i);
                         if ((int)c < nchunk) {
                             load_awq<VEC>(s_row, a_out, c, a[i], st);
-#pragma unroll
-                            for (int v = 0; v < VEC; ++v) x[i][v] = x[i][v] * a[i][v];
                         } else {
 #pragma unroll
                             for (int v = 0; v < VEC; ++v) a[i][v] = 1.0f;
                         }
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int v = 0; v < VEC; ++v) x[r][i][v] = x[r][i][v] * a[i][v];
                     }
                 }
             }
         }
-        uint32_t mx = 0;
 #pragma unroll
-        for (int i = 0; i < NCH; ++i)
-            if (64 * i < nchunk)
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[i][v]) & 0x7FFFFFFFu);   // padding is +0
-        mx = wave_max(mx);
-        if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
-        uint32_t ck = mx;
-        if (SEL && d.rank_top > 1) {
-            auto each = [&](auto&& f) {
+        for (int r = 0; r < R; ++r) {
+            if (r < nrows) {
+                const int64_t row = row0 + r;
+                uint32_t mx = 0;
 #pragma unroll
                 for (int i = 0; i < NCH; ++i)
-                    if (64 * i < nchunk) {
-                        const bool ok = lane + 64 * i < nchunk;
+                    if (64 * i < nchunk)
 #pragma unroll
-                        for (int v = 0; v < VEC; ++v) f(fbits(x[i][v]) & 0x7FFFFFFFu, ok);
+                        for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[r][i][v]) & 0x7FFFFFFFu);   // padding is +0
+                mx = wave_max(mx);
+                if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
+                uint32_t ck = mx;
+                if constexpr (SEL) {
+                    if (d.rank_top > 1) {
+                        auto each = [&](auto&& f) {
+#pragma unroll
+                            for (int i = 0; i < NCH; ++i)
+                                if (64 * i < nchunk) {
+                                    const bool ok = lane + 64 * i < nchunk;
+#pragma unroll
+                                    for (int v = 0; v < VEC; ++v) f(fbits(x[r][i][v]) & 0x7FFFFFFFu, ok);
+                                }
+                        };
+                        ck = kth_largest(each, d.rank_top, hist, lane);
                     }
-            };
-            ck = kth_largest(each, d.rank_top, hist, lane);
-        }
-        uint16_t s16;
-        set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
-        if (lane == 0 && d.scales) gp(d.scales)[row] = s16;
+                }
+                uint16_t s16;
+                set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
+                if (lane == 0 && d.scales) gp(d.scales)[row] = s16;
+                const RowOut ro = row_out(d, row);
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            if (64 * i < nchunk) {
-                const uint32_t c = (uint32_t)(lane + 64 * i);
-                const float (&ai)[VEC] = a[AWQ ? i : 0];
-                chunk_out<MODE, AWQ, VEC>(ro, c, x[i], ai, has_awq, rc, (int)c < nchunk, lane);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < NCH; ++i) {
+                    if (64 * i < nchunk) {
+                        const uint32_t c = (uint32_t)(lane + 64 * i);
+                        const float (&ai)[VEC] = a[AWQ ? i : 0];
+                        chunk_out<MODE, AWQ, VEC>(ro, c, x[r][i], ai, has_awq, rc, (int)c < nchunk, lane);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
             }
         }
-    } else {
+    } else if constexpr (LONG && R == 1) {
         // long row: stream it in pieces; every select pass and the output pass re-read it
+        const int64_t row = row0;
+        const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
+        const RowOut ro = row_out(d, row);
         auto load_chunk = [&](uint32_t c, float (&x)[VEC], float (&a)[VEC], GLB uint16_t* aw) {
             load_x<IN, VEC>(wrow, c * VEC, x);
             if (has_awq) {
@@ -549,19 +579,21 @@ __device__ __forceinline__ void row_quant(const Desc& d, int64_t row, int lane, 
         mx = wave_max(mx);
         if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
         uint32_t ck = mx;
-        if (SEL && d.rank_top > 1) {
-            auto each = [&](auto&& f) {
-                for (int base = 0; base < nchunk; base += 64) {
-                    const uint32_t c = (uint32_t)(base + lane);
-                    if ((int)c < nchunk) {
-                        float x[VEC], a[VEC];
-                        load_chunk(c, x, a, nullptr);
+        if constexpr (SEL) {
+            if (d.rank_top > 1) {
+                auto each = [&](auto&& f) {
+                    for (int base = 0; base < nchunk; base += 64) {
+                        const uint32_t c = (uint32_t)(base + lane);
+                        if ((int)c < nchunk) {
+                            float x[VEC], a[VEC];
+                            load_chunk(c, x, a, nullptr);
 #pragma unroll
-                        for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, true);
+                            for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, true);
+                        }
                     }
-                }
-            };
-            ck = kth_largest(each, d.rank_top, hist, lane);
+                };
+                ck = kth_largest(each, d.rank_top, hist, lane);
+            }
         }
         uint16_t s16;
         set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
@@ -578,6 +610,26 @@ __device__ __forceinline__ void row_quant(const Desc& d, int64_t row, int lane, 
             }
             chunk_out<MODE, AWQ, VEC>(ro, c, x, a, has_awq, rc, ok, lane);
         }
+    }
+}
+
+// Run rows_quant with the group size the host chose for this tensor.
+template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC>
+__device__ __forceinline__ void rows_quant_r(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
+                                             const KArgs& ka, uint32_t& st)
+{
+    constexpr int NCHT = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);
+    switch (d.rgroup) {
+    case 8:
+        if constexpr (NCHT >= 8) { rows_quant<MODE, AWQ, SEL, false, IN, VEC, 8>(d, row0, nrows, lane, hist, ka, st); }
+        break;
+    case 4:
+        if constexpr (NCHT >= 4) { rows_quant<MODE, AWQ, SEL, false, IN, VEC, 4>(d, row0, nrows, lane, hist, ka, st); }
+        break;
+    case 2: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 2>(d, row0, nrows, lane, hist, ka, st); break;
+    default:
+        for (int r = 0; r < nrows; ++r) rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1>(d, row0 + r, 1, lane, hist, ka, st);
+        break;
     }
 }
 
@@ -654,50 +706,89 @@ __device__ __forceinline__ void row_fq_bwd(const Desc& d, int64_t row, int lane)
     }
 }
 
-template <int MODE, bool AWQ, bool SEL>
-__device__ __forceinline__ void dispatch_row(const Desc& d, int64_t row, int lane, uint32_t* hist, const KArgs& ka,
-                                             uint32_t& st)
+template <int MODE, uint32_t F>
+__device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nrows, int lane, uint32_t* hist,
+                                              const KArgs& ka, uint32_t& st)
 {
+    constexpr bool AWQ = (F & F_AWQ) != 0;
+    constexpr bool SEL = (F & F_SEL) != 0;
+    constexpr bool LONG = (F & F_LONG) != 0;
+    constexpr bool SCALAR = (F & F_SCALAR) != 0;
     const bool vec = (d.flags & DF_VEC) != 0;
     if constexpr (MODE == MODE_FQ_BWD) {
-        if (vec) row_fq_bwd<8>(d, row, lane);
-        else row_fq_bwd<1>(d, row, lane);
+        for (int r = 0; r < nrows; ++r) {
+            if (vec) row_fq_bwd<8>(d, row + r, lane);
+            else row_fq_bwd<1>(d, row + r, lane);
+        }
     } else if constexpr (MODE == MODE_FQ) {
-        if (vec) row_quant<MODE_FQ, false, SEL, IN_BF16, 8>(d, row, lane, hist, ka, st);
-        else row_quant<MODE_FQ, false, SEL, IN_BF16, 1>(d, row, lane, hist, ka, st);
+        if constexpr (SCALAR) {
+            if (!vec) { rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 1>(d, row, nrows, lane, hist, ka, st); return; }
+        }
+        rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 8>(d, row, nrows, lane, hist, ka, st);
     } else {
-        if (d.kind == KIND_F16) {
-            if (d.in_dtype == IN_F32) {
-                if (vec) row_passthrough<MODE, IN_F32, 4>(d, row, lane, ka, st);
-                else row_passthrough<MODE, IN_F32, 1>(d, row, lane, ka, st);
-            } else {
-                if (vec) row_passthrough<MODE, IN_BF16, 8>(d, row, lane, ka, st);
-                else row_passthrough<MODE, IN_BF16, 1>(d, row, lane, ka, st);
+        if constexpr ((F & F_PASS) != 0) {
+            if (d.kind == KIND_F16) {
+                if constexpr ((F & F_F32) != 0) {
+                    if (d.in_dtype == IN_F32) {
+                        for (int r = 0; r < nrows; ++r) {
+                            if constexpr (SCALAR) {
+                                if (!vec) { row_passthrough<MODE, IN_F32, 1>(d, row + r, lane, ka, st); continue; }
+                            }
+                            row_passthrough<MODE, IN_F32, 4>(d, row + r, lane, ka, st);
+                        }
+                        return;
+                    }
+                }
+                if constexpr ((F & F_BF16) != 0) {
+                    for (int r = 0; r < nrows; ++r) {
+                        if constexpr (SCALAR) {
+                            if (!vec) { row_passthrough<MODE, IN_BF16, 1>(d, row + r, lane, ka, st); continue; }
+                        }
+                        row_passthrough<MODE, IN_BF16, 8>(d, row + r, lane, ka, st);
+                    }
+                }
+                return;
             }
-        } else if (d.in_dtype == IN_F32) {
-            if (vec) row_quant<MODE, AWQ, SEL, IN_F32, 4>(d, row, lane, hist, ka, st);
-            else row_quant<MODE, AWQ, SEL, IN_F32, 1>(d, row, lane, hist, ka, st);
-        } else {
-            if (vec) row_quant<MODE, AWQ, SEL, IN_BF16, 8>(d, row, lane, hist, ka, st);
-            else row_quant<MODE, AWQ, SEL, IN_BF16, 1>(d, row, lane, hist, ka, st);
+        }
+        if constexpr ((F & F_F32) != 0) {
+            if (d.in_dtype == IN_F32) {
+                if constexpr (SCALAR) {
+                    if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 1>(d, row, nrows, lane, hist, ka, st); return; }
+                }
+                rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 4>(d, row, nrows, lane, hist, ka, st);
+                return;
+            }
+        }
+        if constexpr ((F & F_BF16) != 0) {
+            if constexpr (SCALAR) {
+                if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 1>(d, row, nrows, lane, hist, ka, st); return; }
+            }
+            rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 8>(d, row, nrows, lane, hist, ka, st);
         }
     }
 }
 
-template <int MODE, bool AWQ, bool SEL>
+// A tile is tile_rows consecutive rows of one tensor; wave w takes groups of rgroup rows,
+// groups interleaved over the four waves.
+template <int MODE, uint32_t F>
 __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, int lane, uint32_t* hist,
                                         const KArgs& ka, uint32_t& st)
 {
-    for (int j = 0; j < ka.rows_per_wave; ++j) {
-        const int64_t row = row0 + (int64_t)j * kWaves + wave;
-        if (row < d.rows) dispatch_row<MODE, AWQ, SEL>(d, row, lane, hist, ka, st);
+    const int R = d.rgroup;
+    const int groups = d.tile_rows / (kWaves * R);
+    for (int g = 0; g < groups; ++g) {
+        const int64_t first = row0 + ((int64_t)g * kWaves + wave) * R;
+        if (first < d.rows) {
+            const int nrows = (int)min((int64_t)R, d.rows - first);
+            dispatch_rows<MODE, F>(d, first, nrows, lane, hist, ka, st);
+        }
     }
 }
 
 // Grouped launches read the descriptor table through the restrict-qualified pointers (scalar
-// loads); single-matrix launches take the descriptor from the kernel arguments.  AWQ and SEL
-// (clip below the maximum) are separate instantiations so the common absmax kernel stays lean.
-template <int MODE, bool AWQ, bool SEL>
+// loads); single-matrix launches take the descriptor from the kernel arguments.  F is the
+// feature set compiled in.
+template <int MODE, uint32_t F>
 __global__ void __launch_bounds__(kBlock) pgq_rows_kernel(const TableHeader* __restrict__ hdr,
                                                          const Desc* __restrict__ table,
                                                          const uint32_t* __restrict__ tile_start, KArgs ka)
@@ -713,47 +804,67 @@ __global__ void __launch_bounds__(kBlock) pgq_rows_kernel(const TableHeader* __r
             return;
         }
         // tiles are visited in increasing order, so the owning tensor only moves forward
-        const int64_t rpb = (int64_t)kWaves * ka.rows_per_wave;
         uint32_t di = 0;
         for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x) {
             while (tile >= tile_start[di + 1]) ++di;
-            do_tile<MODE, AWQ, SEL>(table[di], (int64_t)(tile - tile_start[di]) * rpb, wave, lane, hist, ka, st);
+            const Desc& d = table[di];
+            do_tile<MODE, F>(d, (int64_t)(tile - tile_start[di]) * d.tile_rows, wave, lane, hist, ka, st);
         }
     } else {
-        const int64_t rpb = (int64_t)kWaves * ka.rows_per_wave;
         for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x)
-            do_tile<MODE, AWQ, SEL>(ka.single, (int64_t)tile * rpb, wave, lane, hist, ka, st);
+            do_tile<MODE, F>(ka.single, (int64_t)tile * ka.single.tile_rows, wave, lane, hist, ka, st);
     }
     st = wave_or(st);
     if (st && lane == 0 && ka.status) atomicOr(ka.status, st);
 }
 
-template <int MODE, bool AWQ, bool SEL>
-const void* kernel_ptr() { return reinterpret_cast<const void*>(&pgq_rows_kernel<MODE, AWQ, SEL>); }
+template <int MODE, uint32_t F>
+const void* kernel_ptr() { return reinterpret_cast<const void*>(&pgq_rows_kernel<MODE, F>); }
+
+// Instantiations per mode, leanest first; the last covers every feature.
+constexpr uint32_t kExportVariants[] = {F_F32 | F_PASS, F_BF16 | F_PASS, F_F32 | F_PASS | F_AWQ, F_ALL};
+constexpr uint32_t kFqVariants[] = {F_BF16, F_ALL};
 
 template <int MODE>
-const void* pick_mode(bool awq, bool sel)
+const void* export_like(uint32_t v)
 {
-    if (awq) return sel ? kernel_ptr<MODE, true, true>() : kernel_ptr<MODE, true, false>();
-    return sel ? kernel_ptr<MODE, false, true>() : kernel_ptr<MODE, false, false>();
+    switch (v) {
+    case F_F32 | F_PASS: return kernel_ptr<MODE, F_F32 | F_PASS>();
+    case F_BF16 | F_PASS: return kernel_ptr<MODE, F_BF16 | F_PASS>();
+    case F_F32 | F_PASS | F_AWQ: return kernel_ptr<MODE, F_F32 | F_PASS | F_AWQ>();
+    default: return kernel_ptr<MODE, F_ALL>();
+    }
 }
 
-const void* pick(int mode, bool awq, bool sel)
+const void* pick(int mode, uint32_t need)
 {
+    const uint32_t v = variant_of(mode, need);
     switch (mode) {
-    case MODE_EXPORT: return pick_mode<MODE_EXPORT>(awq, sel);
-    case MODE_SQWA: return pick_mode<MODE_SQWA>(awq, sel);
-    case MODE_FQ: return sel ? kernel_ptr<MODE_FQ, false, true>() : kernel_ptr<MODE_FQ, false, false>();
-    case MODE_FQ_BWD: return kernel_ptr<MODE_FQ_BWD, false, false>();
+    case MODE_EXPORT: return export_like<MODE_EXPORT>(v);
+    case MODE_SQWA: return export_like<MODE_SQWA>(v);
+    case MODE_FQ: return v == F_BF16 ? kernel_ptr<MODE_FQ, F_BF16>() : kernel_ptr<MODE_FQ, F_ALL>();
+    case MODE_FQ_BWD: return kernel_ptr<MODE_FQ_BWD, F_ALL>();
     default: return nullptr;
     }
 }
 
 }  // namespace
 
-int launch(int mode, bool awq, bool sel, const KArgs& ka, uint32_t grid, void* stream)
+uint32_t variant_of(int mode, uint32_t need)
 {
-    const void* fn = pick(mode, awq, sel);
+    if (mode == MODE_EXPORT || mode == MODE_SQWA) {
+        for (uint32_t v : kExportVariants)
+            if ((need & ~v) == 0) return v;
+    } else if (mode == MODE_FQ) {
+        for (uint32_t v : kFqVariants)
+            if ((need & ~v) == 0) return v;
+    }
+    return F_ALL;
+}
+
+int launch(int mode, uint32_t need, const KArgs& ka, uint32_t grid, void* stream)
+{
+    const void* fn = pick(mode, need);
     if (!fn || grid == 0) return (int)hipErrorInvalidValue;
     KArgs copy = ka;
     const TableHeader* hdr = ka.hdr;
@@ -763,9 +874,9 @@ int launch(int mode, bool awq, bool sel, const KArgs& ka, uint32_t grid, void* s
     return (int)hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
 }
 
-int max_resident_blocks(int mode, bool awq, bool sel, int* per_cu, int* n_cu)
+int max_resident_blocks(int mode, uint32_t need, int* per_cu, int* n_cu)
 {
-    const void* fn = pick(mode, awq, sel);
+    const void* fn = pick(mode, need);
     if (!fn) return (int)hipErrorInvalidValue;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);

@@ -43,9 +43,5 @@ def same_bits(got: np.ndarray, want: np.ndarray, what: str = ""):
 
 
 def f32_bits_equal(got: np.ndarray, want: np.ndarray, what: str = ""):
-    """Bit equality of float32 arrays, treating +0 and -0 as equal (0 ulp apart)."""
-    g = np.ascontiguousarray(got, dtype=np.float32).copy()
-    w = np.ascontiguousarray(want, dtype=np.float32).copy()
-    g[g == 0] = 0.0
-    w[w == 0] = 0.0
-    same_bits(g, w, what)
+    """Bit equality of float32 arrays, sign of zero included."""
+    same_bits(np.ascontiguousarray(got, dtype=np.float32), np.ascontiguousarray(want, dtype=np.float32), what)

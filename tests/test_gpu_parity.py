@@ -1,7 +1,7 @@
 """GPU parity: libpgq (HIP, gfx950) against the CPU oracle, element by element.
 
-Codes, scales, masks, fp16/bf16 outputs and fp32 dequant/mean values must be bit-identical
-(fp32 compares treat +0 and -0 as equal).  Cases: the five workloads at full size (the
+Codes, scales, masks, fp16/bf16 outputs and fp32 dequant/mean values must be bit-identical,
+sign of zero included.  Cases: the five workloads at full size (the
 oracle checks every output, or sampled tensors where the oracle would take minutes), ragged
 and misaligned shapes, heavy-tailed and long rows, edge rows and status bits.
 """
