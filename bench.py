@@ -13,6 +13,7 @@ its data in the 256 MiB Infinity Cache.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -86,6 +87,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--copies", type=int, default=6, help="input/output sets used in rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="N",
+                    help="after the timed steps, run N plain device copies of 256 MiB (torch copy_) so "
+                         "that hardware byte counters can be scaled against a copy of known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer is "
@@ -96,7 +100,7 @@ def main() -> int:
     import torch
 
     import synth
-    from int6_weight_export_amd import ops
+    from int6_weight_export_amd import ops, pgq
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -114,13 +118,18 @@ def main() -> int:
         sets[i % len(sets)].run()
     torch.cuda.synchronize()
 
+    # Each launch records its own start / stop events from its dispatch (pgq_time_next_launch),
+    # so the pair times the kernel alone, on the stream it runs on, with no extra packets.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:                              # create the underlying HIP events
+        a.record()
+        b.record()
+    handles = [(ctypes.c_void_p(a.cuda_event), ctypes.c_void_p(b.cuda_event)) for a, b in ev]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record()
+        pgq.pgq_time_next_launch(*handles[i])
         sets[i % len(sets)].run()
-        ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in ev]
@@ -178,6 +187,14 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(tensors)
+    if args.copy_calibration:
+        n = (256 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_calibration):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = {"read": 4 * n, "write": 4 * n, "launches": args.copy_calibration}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -204,6 +204,15 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
                                uint32_t flags, uint32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------------------------ */
+/* Timing aid (no method step): the next kernel launch made by this host thread through any    */
+/* pgq_* call records start_event when that kernel begins executing and stop_event when it     */
+/* completes, from the kernel's own dispatch (hipExtLaunchKernel), so the pair times the kernel */
+/* alone.  The events are hipEvent_t handles passed as void* (created by the caller, not       */
+/* owned); NULL, NULL clears a pending request.  Applies to exactly one launch.                */
+/* ------------------------------------------------------------------------------------------ */
+pgq_status pgq_time_next_launch(void* start_event, void* stop_event);
+
+/* ------------------------------------------------------------------------------------------ */
 const char* pgq_status_str(pgq_status s);   /* static string */
 const char* pgq_version(void);              /* static string */
 

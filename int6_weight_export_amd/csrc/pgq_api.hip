@@ -40,11 +40,12 @@ int groups_per_wave()
 // Upper bound on the rows a wavefront processes together.
 int max_rgroup()
 {
-    static const int v = env_int("PGQ_MAX_RGROUP", 8, 1, 8);
+    static const int v = env_int("PGQ_MAX_RGROUP", 1, 1, 8);
     return v;
 }
 
-// Resident workgroups per compute unit for the persistent grid (0 = from the occupancy API).
+// Workgroups per compute unit when the grid is made persistent (0: one workgroup per tile,
+// which lets the hardware dispatcher balance the load; measured faster on MI355X).
 int wg_per_cu_override()
 {
     static const int v = env_int("PGQ_WG_PER_CU", 0, 0, 64);
@@ -88,7 +89,7 @@ size_t esize(int32_t dt) { return dt == PGQ_F32 ? 4 : 2; }
 bool shape_ok(int64_t rows, int64_t cols, int64_t ld)
 {
     if (rows < 0 || cols < 0 || ld < cols) return false;
-    if (cols > ((int64_t)1 << 31) - 64) return false;           // per-row counters are 32-bit
+    if (cols > ((int64_t)1 << 29) - 64) return false;           // a row's byte offsets fit in 32 bits
     if (rows > ((int64_t)1 << 32) - 1) return false;            // tile row origins are 32-bit
     return true;
 }
@@ -145,49 +146,53 @@ struct LimitCache {
 };
 LimitCache g_limits;
 
-uint32_t grid_for(int mode, uint32_t need, uint32_t n_tiles)
+uint32_t grid_for(int mode, uint32_t need, bool table, uint32_t n_tiles)
 {
+    if (wg_per_cu_override() == 0) return std::max<uint32_t>(1, n_tiles);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     int per_cu = 0, ncu = 0;
     {
         std::lock_guard<std::mutex> lk(g_limits.mu);
         if ((int)g_limits.per_cu.size() <= dev) {
-            g_limits.per_cu.resize(dev + 1, std::vector<int>(4 * 128, -1));
+            g_limits.per_cu.resize(dev + 1, std::vector<int>(2 * 4 * 128, -1));
             g_limits.n_cu.resize(dev + 1, -1);
         }
-        int& slot = g_limits.per_cu[dev][mode * 128 + variant_of(mode, need)];
+        int& slot = g_limits.per_cu[dev][(table ? 512 : 0) + mode * 128 + variant_of(mode, need)];
         if (slot < 0 || g_limits.n_cu[dev] < 0) {
             int pc = 0, nc = 0;
-            if (max_resident_blocks(mode, need, &pc, &nc) != 0 || pc <= 0 || nc <= 0) { pc = 4; nc = 256; }
+            if (max_resident_blocks(mode, need, table, &pc, &nc) != 0 || pc <= 0 || nc <= 0) { pc = 4; nc = 256; }
             slot = pc;
             g_limits.n_cu[dev] = nc;
         }
         per_cu = slot;
         ncu = g_limits.n_cu[dev];
     }
-    const int ov = wg_per_cu_override();
-    if (ov > 0) per_cu = ov;
+    per_cu = std::min(per_cu, wg_per_cu_override());
     const uint64_t g = (uint64_t)per_cu * (uint64_t)ncu;
     return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(g, n_tiles));
 }
 
-size_t table_bytes(size_t n_desc)
+size_t table_bytes(size_t n_desc, uint64_t n_tiles)
 {
     return sizeof(TableHeader) + align_up((int64_t)(n_desc * sizeof(Desc)), 64) +
-           (size_t)align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 8);
+           (size_t)align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 64) +
+           (size_t)align_up((int64_t)(n_tiles * sizeof(uint32_t)), 8);
 }
 
-// Rows a wavefront loads together: as many as the register tile holds (a power of two).
+// Rows a wavefront loads together: as many as the register tile holds (a power of two), and
+// the exact chunk count per lane of a row on the vector path.
 void set_grouping(Desc& d, int mode)
 {
     int R = 1;
+    d.nch = 0;
     if (mode != MODE_FQ_BWD && d.kind != KIND_F16 && d.cols > 0) {
         const bool vec = (d.flags & DF_VEC) != 0;
         const int64_t nchunk = vec ? d.cols / (d.in_dtype == IN_F32 ? 4 : 8) : d.cols;
         const int ncht = vec ? (d.in_dtype == IN_F32 ? 8 : 4) : 16;
         const int64_t nch = (nchunk + 63) / 64;
         if (nch <= ncht) {
+            if (vec) d.nch = (int32_t)nch;
             int p2 = 1;
             while (p2 < nch) p2 <<= 1;
             R = std::min(std::min(ncht / p2, 8), max_rgroup());
@@ -198,6 +203,15 @@ void set_grouping(Desc& d, int mode)
     }
     d.rgroup = R;
     d.tile_rows = kWaves * R * groups_per_wave();
+}
+
+// Upper bound on the tiles of a tensor (group size 1), for sizing workspaces before the
+// output pointers, and so the vector path and group size, are known.
+uint64_t max_tiles_for(int64_t rows, int64_t cols)
+{
+    if (rows <= 0 || cols <= 0) return 0;
+    const int64_t tr = (int64_t)kWaves * groups_per_wave();
+    return (uint64_t)((rows + tr - 1) / tr);
 }
 
 uint64_t tiles_for(const Desc& d)
@@ -220,7 +234,7 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs, void* ws, size_
     }
     start[n] = (uint32_t)total;
     if (total == 0) return PGQ_OK;
-    const size_t need = table_bytes(n);
+    const size_t need = table_bytes(n, total);
     if (!ws) return PGQ_ERR_WORKSPACE;
     if (ws_bytes < need) return PGQ_ERR_WORKSPACE;
     if (!aligned(ws, 64)) return PGQ_ERR_ALIGN;
@@ -230,8 +244,12 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs, void* ws, size_
     TableHeader* hdr = reinterpret_cast<TableHeader*>(buf);
     const size_t desc_off = sizeof(TableHeader);
     const size_t start_off = desc_off + align_up((int64_t)(n * sizeof(Desc)), 64);
+    const size_t tdesc_off = start_off + align_up((int64_t)((n + 1) * sizeof(uint32_t)), 64);
     memcpy(buf + desc_off, descs.data(), n * sizeof(Desc));
     memcpy(buf + start_off, start.data(), (n + 1) * sizeof(uint32_t));
+    uint32_t* tdesc = reinterpret_cast<uint32_t*>(buf + tdesc_off);
+    for (size_t i = 0; i < n; ++i)
+        for (uint32_t t = start[i]; t < start[i + 1]; ++t) tdesc[t] = (uint32_t)i;
     uint64_t h = table_hash(buf + desc_off, need - desc_off, 0x243F6A8885A308D3ull ^ (uint64_t)mode);
     h = table_hash(&total, 8, h);
     hdr->magic = kTableMagic;
@@ -249,16 +267,16 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs, void* ws, size_
     ka.hdr = static_cast<const TableHeader*>(ws);
     ka.table = reinterpret_cast<const Desc*>(static_cast<const uint8_t*>(ws) + desc_off);
     ka.tile_start = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(ws) + start_off);
+    ka.tile_desc = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(ws) + tdesc_off);
     ka.checksum = h;
     ka.status = dev_status;
     ka.n_tiles = (uint32_t)total;
     ka.sqwa_k = sqwa_k;
     ka.fq_mode = fq_mode;
-    ka.single = blank_desc();
     uint32_t feats = 0;
     for (const Desc& d : descs) feats |= features_of(d);
-    const uint32_t grid = grid_for(mode, feats, ka.n_tiles);
-    if (launch(mode, feats, ka, grid, stream) != 0) return PGQ_ERR_HIP;
+    const uint32_t grid = grid_for(mode, feats, true, ka.n_tiles);
+    if (launch(mode, feats, ka, nullptr, grid, stream) != 0) return PGQ_ERR_HIP;
     if (hipGetLastError() != hipSuccess) return PGQ_ERR_HIP;
     return PGQ_OK;
 }
@@ -274,10 +292,9 @@ pgq_status run_single(int mode, const Desc& d, uint32_t* dev_status, int sqwa_k,
     ka.n_tiles = (uint32_t)nt;
     ka.sqwa_k = sqwa_k;
     ka.fq_mode = fq_mode;
-    ka.single = d;
     const uint32_t need = features_of(d);
-    const uint32_t grid = grid_for(mode, need, ka.n_tiles);
-    if (launch(mode, need, ka, grid, stream) != 0) return PGQ_ERR_HIP;
+    const uint32_t grid = grid_for(mode, need, false, ka.n_tiles);
+    if (launch(mode, need, ka, &d, grid, stream) != 0) return PGQ_ERR_HIP;
     if (hipGetLastError() != hipSuccess) return PGQ_ERR_HIP;
     return PGQ_OK;
 }
@@ -353,6 +370,12 @@ extern "C" {
 
 const char* pgq_version(void) { return "pgq 0.1 (gfx950)"; }
 
+pgq_status pgq_time_next_launch(void* start_event, void* stop_event)
+{
+    set_timing_events(start_event, stop_event);
+    return PGQ_OK;
+}
+
 const char* pgq_status_str(pgq_status s)
 {
     switch (s) {
@@ -409,9 +432,12 @@ pgq_status pgq_fakequant_workspace(const pgq_fq_tensor* t, int32_t n, size_t* wo
     if (!workspace_bytes) return PGQ_ERR_NULL;
     if (n < 0) return PGQ_ERR_SHAPE;
     if (n > 0 && !t) return PGQ_ERR_NULL;
-    for (int32_t i = 0; i < n; ++i)
+    uint64_t nt = 0;
+    for (int32_t i = 0; i < n; ++i) {
         if (!shape_ok(t[i].rows, t[i].cols, t[i].ld)) return PGQ_ERR_SHAPE;
-    *workspace_bytes = table_bytes((size_t)n);
+        nt += max_tiles_for(t[i].rows, t[i].cols);
+    }
+    *workspace_bytes = table_bytes((size_t)n, nt);
     return PGQ_OK;
 }
 
@@ -483,8 +509,10 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
     if (!qparams_ok(pol->q_default) || !qparams_ok(pol->q_sensitive) || pol->passthrough_below < 0)
         return PGQ_ERR_PARAM;
     int64_t off = 0;
+    uint64_t nt = 0;
     for (int32_t i = 0; i < n; ++i) {
         const pgq_tensor_in& x = t[i];
+        nt += max_tiles_for(x.rows, x.cols);
         pgq_status st = check_tensor_in(x);
         if (st != PGQ_OK) return st;
         pgq_tensor_plan& p = plan[i];
@@ -511,7 +539,7 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
         }
     }
     *arena_bytes = (size_t)std::max<int64_t>(off, 256);
-    *workspace_bytes = table_bytes((size_t)n);
+    *workspace_bytes = table_bytes((size_t)n, nt);
     return PGQ_OK;
 }
 

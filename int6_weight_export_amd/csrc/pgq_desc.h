@@ -1,10 +1,10 @@
 // pgq_desc.h -- descriptors shared by the host layer and the gfx950 kernels of libpgq.
 //
-// A launch processes "tiles": each tile is up to kWaves * rows_per_wave consecutive rows
-// of one tensor.  One wavefront (64 lanes) owns one row at a time.  Grouped calls put a
-// descriptor table (header, one Desc per tensor, then tile_start[n + 1]: the first tile of
-// each tensor, a prefix sum) into the caller's workspace; single-matrix calls pass one
-// Desc by value in the kernel arguments.
+// A launch processes "tiles": each tile is tile_rows consecutive rows of one tensor (four
+// wavefronts, each taking rgroup rows at a time).  Grouped calls put a descriptor table
+// into the caller's workspace: header, one Desc per tensor, tile_start[n + 1] (the first
+// tile of each tensor, a prefix sum) and tile_desc[n_tiles] (the tensor of each tile).
+// Single-matrix calls pass one Desc by value in the kernel arguments.
 #pragma once
 #include <stdint.h>
 
@@ -54,7 +54,7 @@ struct alignas(16) Desc {
     uint32_t flags;           // DF_*
     int32_t rgroup;           // rows a wave processes together (1, 2, 4 or 8)
     int32_t tile_rows;        // rows per tile: kWaves * rgroup * groups per wave
-    int32_t pad;
+    int32_t nch;              // vector path: ceil(chunks / 64) per row, 0 when the row streams
 };
 
 struct alignas(64) TableHeader {
@@ -66,24 +66,27 @@ struct alignas(64) TableHeader {
 };
 
 struct KArgs {
-    const TableHeader* hdr;   // null for a single-matrix launch
+    const TableHeader* hdr;       // grouped launches only (passed as separate kernel arguments)
     const Desc* table;
     const uint32_t* tile_start;   // n_desc + 1 entries
+    const uint32_t* tile_desc;    // n_tiles entries
     uint64_t checksum;
     uint32_t* status;
     uint32_t n_tiles;
-    int32_t reserved;
     int32_t sqwa_k;
-    int32_t fq_mode;          // PGQ_FQ_* for MODE_FQ
-    Desc single;
+    int32_t fq_mode;              // PGQ_FQ_* for MODE_FQ
+    int32_t reserved;
 };
 
 // Host-side launcher implemented next to the kernels.
 // need: the F_* features of the launch.  variant_of() names the instantiation used (its
 // feature set); launch() and max_resident_blocks() take the same `need`.
+// single: the descriptor of a single-matrix launch, or null for a grouped (table) launch.
 uint32_t variant_of(int mode, uint32_t need);
-int launch(int mode, uint32_t need, const KArgs& ka, uint32_t grid, void* stream);
-int max_resident_blocks(int mode, uint32_t need, int* per_cu, int* n_cu);
+int launch(int mode, uint32_t need, const KArgs& ka, const Desc* single, uint32_t grid, void* stream);
+int max_resident_blocks(int mode, uint32_t need, bool table, int* per_cu, int* n_cu);
+// The next launch on this host thread records these hipEvent_t at kernel start / end.
+void set_timing_events(void* start, void* stop);
 
 // Register tile: a row of up to 64 * chunks * elements stays in VGPRs; longer rows stream.
 constexpr int64_t kRegCols_F32 = 64 * 8 * 4;     // 2048

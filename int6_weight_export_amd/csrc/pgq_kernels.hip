@@ -22,6 +22,7 @@
 // "SubSixteen v2" card (PR #69), sections Quantization and Other (6 bits, [-31, 31]);
 // "12L ... Int6AWQ MixedBits" (PR #1495), Submission summary and Mixed-bit details;
 // "Discriminative TTT + SLOT-24" card (PR #1414), Novel Contributions (SQWA).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,99 +91,125 @@ __device__ __forceinline__ void lds_sync_wave()
     __builtin_amdgcn_wave_barrier();
 }
 
-// ---- element loads: VEC consecutive elements at 32-bit element offset e of a row --------------
+// ---- element loads and stores --------------------------------------------------------------
+// Addresses are a uniform (scalar) base plus a 32-bit byte offset per lane, so the hardware's
+// scalar-base addressing applies (a row is shorter than 2^31 bytes).
+template <class T>
+__device__ __forceinline__ const GLB T* at(const GLB void* base, uint32_t byte_off)
+{
+    return reinterpret_cast<const GLB T*>(static_cast<const GLB uint8_t*>(base) + byte_off);
+}
+template <class T>
+__device__ __forceinline__ GLB T* at(GLB void* base, uint32_t byte_off)
+{
+    return reinterpret_cast<GLB T*>(static_cast<GLB uint8_t*>(base) + byte_off);
+}
+
+// A row pointer advanced by a uniform number of elements of the input type.
+template <int IN>
+__device__ __forceinline__ const GLB void* offset_row(const GLB void* row, uint32_t elems)
+{
+    return static_cast<const GLB uint8_t*>(row) + (size_t)elems * (IN == IN_F32 ? 4 : 2);
+}
+
+// Streamed data (weights in, codes / dequant / means / gradients out) is touched once per
+// launch: non-temporal loads and stores keep it from displacing other lines in L2.
+template <class T>
+__device__ __forceinline__ T ldnt(const GLB T* p) { return __builtin_nontemporal_load(p); }
+template <class T>
+__device__ __forceinline__ void stnt(GLB T* p, T v) { __builtin_nontemporal_store(v, p); }
+
+// VEC consecutive elements starting at element e of a row
 template <int IN, int VEC>
 __device__ __forceinline__ void load_x(const GLB void* row, uint32_t e, float (&x)[VEC])
 {
     if constexpr (IN == IN_F32) {
-        const GLB float* p = static_cast<const GLB float*>(row) + e;
         if constexpr (VEC == 4) {
-            const f32x4 v = *reinterpret_cast<const GLB f32x4*>(p);
+            const f32x4 v = ldnt(at<f32x4>(row, e * 4u));
             x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
         } else {
             static_assert(VEC == 1, "fp32 path uses VEC 4 or 1");
-            x[0] = *p;
+            x[0] = ldnt(at<float>(row, e * 4u));
         }
     } else {
-        const GLB uint16_t* p = static_cast<const GLB uint16_t*>(row) + e;
         if constexpr (VEC == 8) {
-            const u32x4 v = *reinterpret_cast<const GLB u32x4*>(p);
+            const u32x4 v = ldnt(at<u32x4>(row, e * 2u));
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) { x[2 * i] = bitsf(w[i] << 16); x[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u); }
         } else {
             static_assert(VEC == 1, "bf16 path uses VEC 8 or 1");
-            x[0] = bitsf((uint32_t)*p << 16);
+            x[0] = bitsf((uint32_t)ldnt(at<uint16_t>(row, e * 2u)) << 16);
         }
     }
 }
 
-// ---- stores / loads of VEC consecutive values --------------------------------------------------
+// int8 codes from integer-valued floats, at element e
 template <int VEC>
-__device__ __forceinline__ void store_codes(GLB int8_t* p, const float (&r)[VEC])
+__device__ __forceinline__ void store_codes(GLB int8_t* base, uint32_t e, const float (&r)[VEC])
 {
     if constexpr (VEC == 1) {
-        *p = (int8_t)(int)r[0];
+        stnt(at<int8_t>(base, e), (int8_t)(int)r[0]);
     } else {
         uint32_t w[VEC / 4];
 #pragma unroll
         for (int i = 0; i < VEC / 4; ++i)
             w[i] = ((uint32_t)(int)r[4 * i] & 0xFFu) | (((uint32_t)(int)r[4 * i + 1] & 0xFFu) << 8) |
                    (((uint32_t)(int)r[4 * i + 2] & 0xFFu) << 16) | (((uint32_t)(int)r[4 * i + 3] & 0xFFu) << 24);
-        if constexpr (VEC == 4) *reinterpret_cast<GLB uint32_t*>(p) = w[0];
-        else *reinterpret_cast<GLB u32x2*>(p) = u32x2{w[0], w[1]};
+        if constexpr (VEC == 4) stnt(at<uint32_t>(base, e), w[0]);
+        else stnt(at<u32x2>(base, e), u32x2{w[0], w[1]});
     }
 }
 
 template <int VEC>
-__device__ __forceinline__ void store_f32(GLB float* p, const float (&v)[VEC])
+__device__ __forceinline__ void store_f32(GLB float* base, uint32_t e, const float (&v)[VEC])
 {
     if constexpr (VEC == 1) {
-        *p = v[0];
+        stnt(at<float>(base, e * 4u), v[0]);
     } else {
 #pragma unroll
         for (int i = 0; i < VEC / 4; ++i)
-            reinterpret_cast<GLB f32x4*>(p)[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+            stnt(at<f32x4>(base, e * 4u + 16u * i), f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]});
     }
 }
 
 template <int VEC>
-__device__ __forceinline__ void load_f32(const GLB float* p, float (&v)[VEC])
+__device__ __forceinline__ void load_f32(const GLB float* base, uint32_t e, float (&v)[VEC])
 {
     if constexpr (VEC == 1) {
-        v[0] = *p;
+        v[0] = ldnt(at<float>(base, e * 4u));
     } else {
 #pragma unroll
         for (int i = 0; i < VEC / 4; ++i) {
-            const f32x4 t = reinterpret_cast<const GLB f32x4*>(p)[i];
+            const f32x4 t = ldnt(at<f32x4>(base, e * 4u + 16u * i));
             v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
         }
     }
 }
 
-// 16-bit values (fp16 or bf16 bit patterns) packed two per dword
+// 16-bit values (fp16 or bf16 bit patterns) packed two per dword, at element e
 template <int VEC>
-__device__ __forceinline__ void store_u16(GLB uint16_t* p, const uint16_t (&h)[VEC])
+__device__ __forceinline__ void store_u16(GLB uint16_t* base, uint32_t e, const uint16_t (&h)[VEC])
 {
     if constexpr (VEC == 1) {
-        *p = h[0];
+        stnt(at<uint16_t>(base, e * 2u), h[0]);
     } else {
         uint32_t w[VEC / 2];
 #pragma unroll
         for (int i = 0; i < VEC / 2; ++i) w[i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
-        if constexpr (VEC == 4) *reinterpret_cast<GLB u32x2*>(p) = u32x2{w[0], w[1]};
-        else *reinterpret_cast<GLB u32x4*>(p) = u32x4{w[0], w[1], w[2], w[3]};
+        if constexpr (VEC == 4) stnt(at<u32x2>(base, e * 2u), u32x2{w[0], w[1]});
+        else stnt(at<u32x4>(base, e * 2u), u32x4{w[0], w[1], w[2], w[3]});
     }
 }
 
 template <int VEC>
-__device__ __forceinline__ void load_u16(const GLB uint16_t* p, uint16_t (&h)[VEC])
+__device__ __forceinline__ void load_u16(const GLB uint16_t* base, uint32_t e, uint16_t (&h)[VEC])
 {
     if constexpr (VEC == 1) {
-        h[0] = *p;
+        h[0] = ldnt(at<uint16_t>(base, e * 2u));
     } else {
         static_assert(VEC == 8, "16-bit vector loads are 8 wide");
-        const u32x4 v = *reinterpret_cast<const GLB u32x4*>(p);
+        const u32x4 v = ldnt(at<u32x4>(base, e * 2u));
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) { h[2 * i] = (uint16_t)(w[i] & 0xFFFF); h[2 * i + 1] = (uint16_t)(w[i] >> 16); }
@@ -340,13 +367,17 @@ __device__ __forceinline__ RowOut row_out(const Desc& d, int64_t row)
     return ro;
 }
 
-// ---- outputs of one chunk: VEC consecutive elements at element offset c * VEC of the row ------
+// ---- outputs of one chunk: lane l owns VEC elements at (cu + l) * VEC of the row -------------
+// cu is uniform: it moves the scalar base pointers, and every lane adds the same small offset
+// lane * VEC, so all chunks of a row share one offset register.
 template <int MODE, bool AWQ, int VEC>
-__device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t c, const float (&x)[VEC],
+__device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const float (&x)[VEC],
                                           const float (&a)[VEC], bool has_awq, const RowCtx& rc,
                                           bool valid, int lane)
 {
-    const uint32_t e = c * VEC;
+    const uint32_t c = cu + (uint32_t)lane;
+    const uint32_t eu = cu * VEC;                 // uniform element offset of the chunk group
+    const uint32_t e = (uint32_t)lane * VEC;      // lane's element offset within it
     float r[VEC];
     quant_chunk<VEC>(x, rc, r);
     float dq[VEC];
@@ -359,32 +390,32 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t c, const fl
     }
     if constexpr (MODE == MODE_EXPORT) {
         if (!valid) return;
-        if (ro.codes) store_codes<VEC>(ro.codes + e, r);
+        if (ro.codes) store_codes<VEC>(ro.codes + eu, e, r);
         if (ro.dq) {
             if (ro.dq_f32) {
-                store_f32<VEC>(static_cast<GLB float*>(ro.dq) + e, dq);
+                store_f32<VEC>(static_cast<GLB float*>(ro.dq) + eu, e, dq);
             } else {
                 uint16_t h[VEC];
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) h[v] = f2bf(dq[v]);
-                store_u16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + e, h);
+                store_u16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + eu, e, h);
             }
         }
     } else if constexpr (MODE == MODE_SQWA) {
         if (!valid) return;
-        GLB float* mp = ro.mean + e;
+        GLB float* mp = ro.mean + eu;
         if (rc.k == 1) {
-            store_f32<VEC>(mp, dq);
+            store_f32<VEC>(mp, e, dq);
         } else {
             float m[VEC];
-            load_f32<VEC>(mp, m);
+            load_f32<VEC>(mp, e, m);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 const float diff = dq[v] - m[v];
                 const float step = diff / rc.kf;
                 m[v] = m[v] + step;
             }
-            store_f32<VEC>(mp, m);
+            store_f32<VEC>(mp, e, m);
         }
     } else if constexpr (MODE == MODE_FQ) {
         bool keep[VEC];
@@ -397,39 +428,40 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t c, const fl
                     uint32_t byte = 0;
 #pragma unroll
                     for (int v = 0; v < 8; ++v) byte |= keep[v] ? (1u << v) : 0u;
-                    ro.mask[c] = (uint8_t)byte;
+                    *at<uint8_t>(ro.mask + cu, (uint32_t)lane) = (uint8_t)byte;
                 }
             } else {
                 // element c = 64 * i + lane: the 64 lanes give 8 whole mask bytes
                 const uint64_t bal = __ballot(valid && keep[0]);
-                const uint32_t byte0 = (c - (uint32_t)lane) >> 3;
+                const uint32_t byte0 = cu >> 3;
                 // lane b < 8 writes byte b of the group when that byte holds an element of the row
                 const bool own = __shfl(valid ? 1 : 0, 8 * (lane & 7), 64) != 0;
-                if (lane < 8 && own) ro.mask[byte0 + lane] = (uint8_t)(bal >> (8 * lane));
+                if (lane < 8 && own) *at<uint8_t>(ro.mask + byte0, (uint32_t)lane) = (uint8_t)(bal >> (8 * lane));
             }
         }
         if (!valid) return;
         uint16_t h[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) h[v] = f2bf(dq[v]);
-        if (ro.dq) store_u16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + e, h);
-        if (ro.codes) store_codes<VEC>(ro.codes + e, r);
+        if (ro.dq) store_u16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + eu, e, h);
+        if (ro.codes) store_codes<VEC>(ro.codes + eu, e, r);
         if (rc.fq_mode == PGQ_FQ_FWD_BWD) {
             uint16_t g[VEC];
-            load_u16<VEC>(ro.grad + e, g);
+            load_u16<VEC>(ro.grad + eu, e, g);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) g[v] = keep[v] ? g[v] : (uint16_t)0;
-            store_u16<VEC>(ro.gout + e, g);
+            store_u16<VEC>(ro.gout + eu, e, g);
         }
     }
 }
 
+// AWQ multipliers of lane l's columns in chunk group cu (cu uniform)
 template <int VEC>
-__device__ __forceinline__ void load_awq(const GLB float* s_row, GLB uint16_t* a_out, uint32_t c,
+__device__ __forceinline__ void load_awq(const GLB float* s_row, GLB uint16_t* a_out, uint32_t cu, int lane,
                                          float (&a)[VEC], uint32_t& st)
 {
     float s[VEC];
-    load_f32<VEC>(s_row + c * VEC, s);
+    load_f32<VEC>(s_row + cu * VEC, (uint32_t)lane * VEC, s);
     uint16_t h[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
@@ -437,20 +469,21 @@ __device__ __forceinline__ void load_awq(const GLB float* s_row, GLB uint16_t* a
         h[v] = f2h(__builtin_sqrtf(s[v]));       // correctly rounded sqrt, then fp16
         a[v] = h2f(h[v]);
     }
-    if (a_out) store_u16<VEC>(a_out + c * VEC, h);
+    if (a_out) store_u16<VEC>(a_out + cu * VEC, (uint32_t)lane * VEC, h);
 }
 
 // ---- a group of R consecutive rows of one tensor (integer kinds) ------------------------------
 // The register tile holds NCHT chunks per lane.  A row needing NCHT / R chunks or fewer is
 // processed R rows at a time: every row's loads are issued before the first reduction, so a
 // wave keeps R rows in flight.  Rows longer than the tile (R = 1 only) stream in pieces.
-template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R>
+// EXACT: NCH is exactly ceil(chunks / 64) for this tensor, so chunks 0 .. NCH-2 are full and
+// only the last needs a per-lane bound; otherwise NCH is the tile share and chunks are guarded.
+template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R, int NCH, bool EXACT>
 __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
                                            const KArgs& ka, uint32_t& st)
 {
     constexpr int NCHT = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);   // register tile, chunks per lane
-    constexpr int NCH = NCHT / R;                                       // chunks per lane per row
-    static_assert(NCH * R == NCHT, "R divides the register tile");
+    static_assert(NCH * R <= NCHT, "the group fits the register tile");
     static_assert(64 * NCHT * VEC == (VEC == 1 ? kRegCols_Scalar : (IN == IN_F32 ? kRegCols_F32 : kRegCols_BF16)),
                   "register tile must match the host's long-row threshold");
     const int nchunk = (int)(d.cols / VEC);
@@ -467,6 +500,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
     rc.fq_mode = ka.fq_mode;
 
     if (R > 1 || !LONG || nchunk <= 64 * NCH) {
+        static_assert(!EXACT || !LONG, "exact-width groups never stream");
         float x[R][NCH][VEC];
         float a[AWQ ? NCH : 1][VEC];
 #pragma unroll
@@ -475,10 +509,10 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)((row0 + r) * d.ld) * esz;
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
-                    if (64 * i < nchunk) {
+                    if (EXACT || 64 * i < nchunk) {
                         const uint32_t c = (uint32_t)(lane + 64 * i);
-                        if ((int)c < nchunk) {
-                            load_x<IN, VEC>(wrow, c * VEC, x[r][i]);
+                        if ((EXACT && i < NCH - 1) || (int)c < nchunk) {
+                            load_x<IN, VEC>(offset_row<IN>(wrow, 64u * i * VEC), (uint32_t)lane * VEC, x[r][i]);
                         } else {
 #pragma unroll
                             for (int v = 0; v < VEC; ++v) x[r][i][v] = 0.0f;
@@ -492,10 +526,10 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 // the column multipliers are the same for every row of the group
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
-                    if (64 * i < nchunk) {
+                    if (EXACT || 64 * i < nchunk) {
                         const uint32_t c = (uint32_t)(lane + 64 * i);
-                        if ((int)c < nchunk) {
-                            load_awq<VEC>(s_row, a_out, c, a[i], st);
+                        if ((EXACT && i < NCH - 1) || (int)c < nchunk) {
+                            load_awq<VEC>(s_row, a_out, 64u * i, lane, a[i], st);
                         } else {
 #pragma unroll
                             for (int v = 0; v < VEC; ++v) a[i][v] = 1.0f;
@@ -515,7 +549,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 uint32_t mx = 0;
 #pragma unroll
                 for (int i = 0; i < NCH; ++i)
-                    if (64 * i < nchunk)
+                    if (EXACT || 64 * i < nchunk)
 #pragma unroll
                         for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[r][i][v]) & 0x7FFFFFFFu);   // padding is +0
                 mx = wave_max(mx);
@@ -526,8 +560,8 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                         auto each = [&](auto&& f) {
 #pragma unroll
                             for (int i = 0; i < NCH; ++i)
-                                if (64 * i < nchunk) {
-                                    const bool ok = lane + 64 * i < nchunk;
+                                if (EXACT || 64 * i < nchunk) {
+                                    const bool ok = (EXACT && i < NCH - 1) || lane + 64 * i < nchunk;
 #pragma unroll
                                     for (int v = 0; v < VEC; ++v) f(fbits(x[r][i][v]) & 0x7FFFFFFFu, ok);
                                 }
@@ -541,10 +575,11 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 const RowOut ro = row_out(d, row);
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
-                    if (64 * i < nchunk) {
+                    if (EXACT || 64 * i < nchunk) {
                         const uint32_t c = (uint32_t)(lane + 64 * i);
                         const float (&ai)[VEC] = a[AWQ ? i : 0];
-                        chunk_out<MODE, AWQ, VEC>(ro, c, x[r][i], ai, has_awq, rc, (int)c < nchunk, lane);
+                        const bool ok = (EXACT && i < NCH - 1) || (int)c < nchunk;
+                        chunk_out<MODE, AWQ, VEC>(ro, 64u * i, x[r][i], ai, has_awq, rc, ok, lane);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -555,10 +590,11 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         const int64_t row = row0;
         const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
         const RowOut ro = row_out(d, row);
-        auto load_chunk = [&](uint32_t c, float (&x)[VEC], float (&a)[VEC], GLB uint16_t* aw) {
-            load_x<IN, VEC>(wrow, c * VEC, x);
+        // cu: uniform chunk base of the piece; lane l takes chunk cu + l
+        auto load_chunk = [&](uint32_t cu, float (&x)[VEC], float (&a)[VEC], GLB uint16_t* aw) {
+            load_x<IN, VEC>(offset_row<IN>(wrow, cu * VEC), (uint32_t)lane * VEC, x);
             if (has_awq) {
-                load_awq<VEC>(s_row, aw, c, a, st);
+                load_awq<VEC>(s_row, aw, cu, lane, a, st);
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) x[v] = x[v] * a[v];
             } else {
@@ -571,7 +607,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
             const uint32_t c = (uint32_t)(base + lane);
             if ((int)c < nchunk) {
                 float x[VEC], a[VEC];
-                load_chunk(c, x, a, a_out);
+                load_chunk((uint32_t)base, x, a, a_out);
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[v]) & 0x7FFFFFFFu);
             }
@@ -586,7 +622,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                         const uint32_t c = (uint32_t)(base + lane);
                         if ((int)c < nchunk) {
                             float x[VEC], a[VEC];
-                            load_chunk(c, x, a, nullptr);
+                            load_chunk((uint32_t)base, x, a, nullptr);
 #pragma unroll
                             for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, true);
                         }
@@ -603,33 +639,86 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
             const bool ok = (int)c < nchunk;
             float x[VEC], a[VEC];
             if (ok) {
-                load_chunk(c, x, a, nullptr);
+                load_chunk((uint32_t)base, x, a, nullptr);
             } else {
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) { x[v] = 0.0f; a[v] = 1.0f; }
             }
-            chunk_out<MODE, AWQ, VEC>(ro, c, x, a, has_awq, rc, ok, lane);
+            chunk_out<MODE, AWQ, VEC>(ro, (uint32_t)base, x, a, has_awq, rc, ok, lane);
         }
     }
 }
 
-// Run rows_quant with the group size the host chose for this tensor.
+// Run rows_quant with the group shape the host chose for this tensor.  Vector paths use the
+// exact chunk count (d.nch) and group size (d.rgroup); the element-wise path splits the tile.
+template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R, int NCH>
+__device__ __forceinline__ void rows_exact(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
+                                           const KArgs& ka, uint32_t& st)
+{
+    rows_quant<MODE, AWQ, SEL, false, IN, VEC, R, NCH, true>(d, row0, nrows, lane, hist, ka, st);
+}
+
 template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC>
 __device__ __forceinline__ void rows_quant_r(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
                                              const KArgs& ka, uint32_t& st)
 {
     constexpr int NCHT = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);
-    switch (d.rgroup) {
-    case 8:
-        if constexpr (NCHT >= 8) { rows_quant<MODE, AWQ, SEL, false, IN, VEC, 8>(d, row0, nrows, lane, hist, ka, st); }
-        break;
-    case 4:
-        if constexpr (NCHT >= 4) { rows_quant<MODE, AWQ, SEL, false, IN, VEC, 4>(d, row0, nrows, lane, hist, ka, st); }
-        break;
-    case 2: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 2>(d, row0, nrows, lane, hist, ka, st); break;
-    default:
-        for (int r = 0; r < nrows; ++r) rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1>(d, row0 + r, 1, lane, hist, ka, st);
-        break;
+    if constexpr (VEC == 1) {
+        switch (d.rgroup) {
+        case 8: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 8, NCHT / 8, false>(d, row0, nrows, lane, hist, ka, st); break;
+        case 4: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 4, NCHT / 4, false>(d, row0, nrows, lane, hist, ka, st); break;
+        case 2: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 2, NCHT / 2, false>(d, row0, nrows, lane, hist, ka, st); break;
+        default:
+            for (int r = 0; r < nrows; ++r)
+                rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, ka, st);
+            break;
+        }
+        return;
+    } else {
+        // (rgroup, nch) pairs the host produces: rgroup = NCHT / pow2ceil(nch), or 1
+        const int key = d.rgroup * 16 + d.nch;
+        if (d.nch == 0) {            // longer than the register tile: stream row by row
+            if constexpr (LONG) {
+                for (int r = 0; r < nrows; ++r)
+                    rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, ka, st);
+            }
+            return;
+        }
+        if constexpr (NCHT == 8) {
+            switch (key) {
+            case 8 * 16 + 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 8, 1>(d, row0, nrows, lane, hist, ka, st); return;
+            case 4 * 16 + 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 4, 2>(d, row0, nrows, lane, hist, ka, st); return;
+            case 2 * 16 + 3: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 3>(d, row0, nrows, lane, hist, ka, st); return;
+            case 2 * 16 + 4: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 4>(d, row0, nrows, lane, hist, ka, st); return;
+            default: break;
+            }
+        } else {
+            switch (key) {
+            case 4 * 16 + 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 4, 1>(d, row0, nrows, lane, hist, ka, st); return;
+            case 2 * 16 + 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 2>(d, row0, nrows, lane, hist, ka, st); return;
+            default: break;
+            }
+        }
+        // one row at a time with its exact chunk count
+        for (int r = 0; r < nrows; ++r) {
+            const int64_t row = row0 + r;
+            switch (d.nch) {
+            case 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 1>(d, row, 1, lane, hist, ka, st); break;
+            case 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 2>(d, row, 1, lane, hist, ka, st); break;
+            case 3: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 3>(d, row, 1, lane, hist, ka, st); break;
+            case 4: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 4>(d, row, 1, lane, hist, ka, st); break;
+            default:
+                if constexpr (NCHT == 8) {
+                    switch (d.nch) {
+                    case 5: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 5>(d, row, 1, lane, hist, ka, st); break;
+                    case 6: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 6>(d, row, 1, lane, hist, ka, st); break;
+                    case 7: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 7>(d, row, 1, lane, hist, ka, st); break;
+                    default: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 8>(d, row, 1, lane, hist, ka, st); break;
+                    }
+                }
+                break;
+            }
+        }
     }
 }
 
@@ -661,22 +750,21 @@ __device__ __forceinline__ void row_passthrough(const Desc& d, int64_t row, int 
             else if ((h[v] & 0x7FFFu) == 0x7C00u) st |= PGQ_DEV_F16_OVF;
         }
         if constexpr (MODE == MODE_EXPORT) {
-            if (hrow) store_u16<VEC>(hrow + e, h);
-            if (dqrow) store_f32<VEC>(dqrow + e, y);
+            if (hrow) store_u16<VEC>(hrow, e, h);
+            if (dqrow) store_f32<VEC>(dqrow, e, y);
         } else {
-            GLB float* mp = mrow + e;
             if (ka.sqwa_k == 1) {
-                store_f32<VEC>(mp, y);
+                store_f32<VEC>(mrow, e, y);
             } else {
                 float m[VEC];
-                load_f32<VEC>(mp, m);
+                load_f32<VEC>(mrow, e, m);
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) {
                     const float diff = y[v] - m[v];
                     const float step = diff / kf;
                     m[v] = m[v] + step;
                 }
-                store_f32<VEC>(mp, m);
+                store_f32<VEC>(mrow, e, m);
             }
         }
     }
@@ -693,7 +781,7 @@ __device__ __forceinline__ void row_fq_bwd(const Desc& d, int64_t row, int lane)
         if ((int)c >= nchunk) break;
         const uint32_t e = c * VEC;
         uint16_t g[VEC];
-        load_u16<VEC>(ro.grad + e, g);
+        load_u16<VEC>(ro.grad, e, g);
         if constexpr (VEC == 8) {
             const uint32_t byte = ro.mask[c];
 #pragma unroll
@@ -702,7 +790,7 @@ __device__ __forceinline__ void row_fq_bwd(const Desc& d, int64_t row, int lane)
             const uint32_t byte = ro.mask[c >> 3];
             g[0] = ((byte >> (c & 7u)) & 1u) ? g[0] : (uint16_t)0;
         }
-        store_u16<VEC>(ro.gout + e, g);
+        store_u16<VEC>(ro.gout, e, g);
     }
 }
 
@@ -785,65 +873,108 @@ __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, i
     }
 }
 
-// Grouped launches read the descriptor table through the restrict-qualified pointers (scalar
-// loads); single-matrix launches take the descriptor from the kernel arguments.  F is the
-// feature set compiled in.
+// Copy the descriptor fields a mode uses into scalar registers in one round of scalar loads.
+// Scalar loads return out of order, so each use waits for every outstanding one; loading all
+// fields before the first branch (the empty asm consumes them) avoids a chain of dependent
+// load rounds before the first row load.
 template <int MODE, uint32_t F>
-__global__ void __launch_bounds__(kBlock) pgq_rows_kernel(const TableHeader* __restrict__ hdr,
-                                                         const Desc* __restrict__ table,
-                                                         const uint32_t* __restrict__ tile_start, KArgs ka)
+__device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
+{
+    Desc d = *p;
+    asm volatile("" ::"s"(d.rows), "s"(d.cols), "s"(d.ld), "s"(d.kind), "s"(d.flags), "s"(d.rgroup),
+                 "s"(d.tile_rows), "s"(d.nch), "s"(d.w), "s"(d.Q));
+    if constexpr (MODE == MODE_EXPORT) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.dq_dtype));
+    if constexpr (MODE == MODE_SQWA) asm volatile("" ::"s"(d.mean));
+    if constexpr (MODE == MODE_FQ || MODE == MODE_FQ_BWD)
+        asm volatile("" ::"s"(d.dq), "s"(d.scales), "s"(d.mask), "s"(d.grad), "s"(d.grad_out));
+    if constexpr ((F & F_PASS) != 0 && MODE == MODE_EXPORT) asm volatile("" ::"s"(d.f16_out));
+    if constexpr ((F & F_SEL) != 0) asm volatile("" ::"s"(d.rank_top));
+    if constexpr ((F & F_AWQ) != 0) asm volatile("" ::"s"(d.awq_s), "s"(d.awq_out));
+    return d;
+}
+
+// Grouped launches: descriptors come from the table in the workspace through restrict-qualified
+// pointers (read-only for the whole launch, so scalar loads).  F is the feature set compiled in.
+template <int MODE, uint32_t F>
+__global__ void __launch_bounds__(kBlock) pgq_table_kernel(const TableHeader* __restrict__ hdr,
+                                                          const Desc* __restrict__ table,
+                                                          const uint32_t* __restrict__ tile_start,
+                                                          const uint32_t* __restrict__ tile_desc, KArgs ka)
+{
+    __shared__ uint32_t hist_all[kWaves][256];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    uint32_t* hist = hist_all[wave];
+    // round 1: the header and this tile's tensor (tile_desc lies inside the workspace whatever
+    // it holds); round 2, only for a valid table: that tensor's descriptor.  The owning tensor
+    // of the next tile (persistent grids) is fetched one tile ahead.
+    uint32_t tile = blockIdx.x;
+    const uint64_t magic = hdr->magic;
+    const uint64_t checksum = hdr->checksum;
+    uint32_t di = tile < ka.n_tiles ? tile_desc[tile] : 0;
+    if (magic != kTableMagic || checksum != ka.checksum) {
+        if (threadIdx.x == 0 && ka.status) atomicOr(ka.status, PGQ_DEV_STALE_TABLE);
+        return;
+    }
+    uint32_t st = 0;
+    while (tile < ka.n_tiles) {
+        const uint32_t next = tile + gridDim.x;
+        const uint32_t ndi = next < ka.n_tiles ? tile_desc[next] : 0;
+        const uint32_t first = tile_start[di];
+        const Desc d = fetch_desc<MODE, F>(table + di);
+        do_tile<MODE, F>(d, (int64_t)(tile - first) * d.tile_rows, wave, lane, hist, ka, st);
+        tile = next;
+        di = ndi;
+    }
+    st = wave_or(st);
+    if (st && lane == 0 && ka.status) atomicOr(ka.status, st);
+}
+
+// Single-matrix launches: the descriptor is a kernel argument.
+template <int MODE, uint32_t F>
+__global__ void __launch_bounds__(kBlock) pgq_single_kernel(const Desc d, KArgs ka)
 {
     __shared__ uint32_t hist_all[kWaves][256];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     uint32_t* hist = hist_all[wave];
     uint32_t st = 0;
-    if (hdr) {
-        if (hdr->magic != kTableMagic || hdr->checksum != ka.checksum) {
-            if (threadIdx.x == 0 && ka.status) atomicOr(ka.status, PGQ_DEV_STALE_TABLE);
-            return;
-        }
-        // tiles are visited in increasing order, so the owning tensor only moves forward
-        uint32_t di = 0;
-        for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x) {
-            while (tile >= tile_start[di + 1]) ++di;
-            const Desc& d = table[di];
-            do_tile<MODE, F>(d, (int64_t)(tile - tile_start[di]) * d.tile_rows, wave, lane, hist, ka, st);
-        }
-    } else {
-        for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x)
-            do_tile<MODE, F>(ka.single, (int64_t)tile * ka.single.tile_rows, wave, lane, hist, ka, st);
-    }
+    for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x)
+        do_tile<MODE, F>(d, (int64_t)tile * d.tile_rows, wave, lane, hist, ka, st);
     st = wave_or(st);
     if (st && lane == 0 && ka.status) atomicOr(ka.status, st);
 }
 
 template <int MODE, uint32_t F>
-const void* kernel_ptr() { return reinterpret_cast<const void*>(&pgq_rows_kernel<MODE, F>); }
+const void* kernel_ptr(bool table)
+{
+    return table ? reinterpret_cast<const void*>(&pgq_table_kernel<MODE, F>)
+                 : reinterpret_cast<const void*>(&pgq_single_kernel<MODE, F>);
+}
 
 // Instantiations per mode, leanest first; the last covers every feature.
 constexpr uint32_t kExportVariants[] = {F_F32 | F_PASS, F_BF16 | F_PASS, F_F32 | F_PASS | F_AWQ, F_ALL};
 constexpr uint32_t kFqVariants[] = {F_BF16, F_ALL};
 
 template <int MODE>
-const void* export_like(uint32_t v)
+const void* export_like(uint32_t v, bool table)
 {
     switch (v) {
-    case F_F32 | F_PASS: return kernel_ptr<MODE, F_F32 | F_PASS>();
-    case F_BF16 | F_PASS: return kernel_ptr<MODE, F_BF16 | F_PASS>();
-    case F_F32 | F_PASS | F_AWQ: return kernel_ptr<MODE, F_F32 | F_PASS | F_AWQ>();
-    default: return kernel_ptr<MODE, F_ALL>();
+    case F_F32 | F_PASS: return kernel_ptr<MODE, F_F32 | F_PASS>(table);
+    case F_BF16 | F_PASS: return kernel_ptr<MODE, F_BF16 | F_PASS>(table);
+    case F_F32 | F_PASS | F_AWQ: return kernel_ptr<MODE, F_F32 | F_PASS | F_AWQ>(table);
+    default: return kernel_ptr<MODE, F_ALL>(table);
     }
 }
 
-const void* pick(int mode, uint32_t need)
+const void* pick(int mode, uint32_t need, bool table)
 {
     const uint32_t v = variant_of(mode, need);
     switch (mode) {
-    case MODE_EXPORT: return export_like<MODE_EXPORT>(v);
-    case MODE_SQWA: return export_like<MODE_SQWA>(v);
-    case MODE_FQ: return v == F_BF16 ? kernel_ptr<MODE_FQ, F_BF16>() : kernel_ptr<MODE_FQ, F_ALL>();
-    case MODE_FQ_BWD: return kernel_ptr<MODE_FQ_BWD, F_ALL>();
+    case MODE_EXPORT: return export_like<MODE_EXPORT>(v, table);
+    case MODE_SQWA: return export_like<MODE_SQWA>(v, table);
+    case MODE_FQ: return v == F_BF16 ? kernel_ptr<MODE_FQ, F_BF16>(table) : kernel_ptr<MODE_FQ, F_ALL>(table);
+    case MODE_FQ_BWD: return kernel_ptr<MODE_FQ_BWD, F_ALL>(table);
     default: return nullptr;
     }
 }
@@ -862,21 +993,49 @@ uint32_t variant_of(int mode, uint32_t need)
     return F_ALL;
 }
 
-int launch(int mode, uint32_t need, const KArgs& ka, uint32_t grid, void* stream)
+namespace {
+thread_local hipEvent_t t_start = nullptr;   // pgq_time_next_launch
+thread_local hipEvent_t t_stop = nullptr;
+
+hipError_t launch_args(const void* fn, uint32_t grid, void** args, hipStream_t s)
 {
-    const void* fn = pick(mode, need);
+    if (t_start || t_stop) {
+        hipEvent_t a = t_start, b = t_stop;
+        t_start = t_stop = nullptr;
+        return hipExtLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, s, a, b, 0);
+    }
+    return hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, s);
+}
+}  // namespace
+
+void set_timing_events(void* start, void* stop)
+{
+    t_start = static_cast<hipEvent_t>(start);
+    t_stop = static_cast<hipEvent_t>(stop);
+}
+
+int launch(int mode, uint32_t need, const KArgs& ka, const Desc* single, uint32_t grid, void* stream)
+{
+    const void* fn = pick(mode, need, single == nullptr);
     if (!fn || grid == 0) return (int)hipErrorInvalidValue;
     KArgs copy = ka;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (single) {
+        Desc d = *single;
+        void* args[] = {&d, &copy};
+        return (int)launch_args(fn, grid, args, s);
+    }
     const TableHeader* hdr = ka.hdr;
     const Desc* table = ka.table;
     const uint32_t* tile_start = ka.tile_start;
-    void* args[] = {&hdr, &table, &tile_start, &copy};
-    return (int)hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
+    const uint32_t* tile_desc = ka.tile_desc;
+    void* args[] = {&hdr, &table, &tile_start, &tile_desc, &copy};
+    return (int)launch_args(fn, grid, args, s);
 }
 
-int max_resident_blocks(int mode, uint32_t need, int* per_cu, int* n_cu)
+int max_resident_blocks(int mode, uint32_t need, bool table, int* per_cu, int* n_cu)
 {
-    const void* fn = pick(mode, need);
+    const void* fn = pick(mode, need, table);
     if (!fn) return (int)hipErrorInvalidValue;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);

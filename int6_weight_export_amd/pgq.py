@@ -90,6 +90,7 @@ SIGNATURES = {
                                 ctypes.POINTER(_P), _P, _SZ, _U32, _P, _P]),
     "pgq_sqwa_accumulate": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan),
                                    ctypes.POINTER(_P), _I32, _P, _SZ, _U32, _P, _P]),
+    "pgq_time_next_launch": (_I32, [_P, _P]),
     "pgq_status_str": (ctypes.c_char_p, [_I32]),
     "pgq_version": (ctypes.c_char_p, []),
 }
@@ -136,6 +137,10 @@ def pgq_export_model(t, n, plan, arena, dq_out, workspace, workspace_bytes, flag
 def pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status, stream):
     return _lib.pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status,
                                     stream)
+
+
+def pgq_time_next_launch(start_event, stop_event):
+    return _lib.pgq_time_next_launch(start_event, stop_event)
 
 
 def pgq_status_str(s: int) -> str:

@@ -85,8 +85,7 @@ def test_fakequant_argument_errors():
     assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD, t2, 2, q(), None, 0, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
     need = ctypes.c_size_t(0)
     assert pgq.pgq_fakequant_workspace(t2, 2, ctypes.byref(need)) == pgq.PGQ_OK and need.value > 0
-    assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD, t2, 2, q(), FAKE, need.value - 8, 0, None,
-                                     None) == pgq.PGQ_ERR_WORKSPACE
+    assert pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD, t2, 2, q(), FAKE, 64, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
 
 
 def _tensor_array(ts, awq=False):
@@ -165,8 +164,7 @@ def test_export_and_sqwa_argument_errors():
     assert pgq.pgq_export_model(arr, 3, plan, None, None, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_NULL
     assert pgq.pgq_export_model(arr, 3, plan, FAKE + 64, None, FAKE, wb.value, 0, None,
                                 None) == pgq.PGQ_ERR_ALIGN
-    assert pgq.pgq_export_model(arr, 3, plan, FAKE, None, FAKE, wb.value - 8, 0, None,
-                                None) == pgq.PGQ_ERR_WORKSPACE
+    assert pgq.pgq_export_model(arr, 3, plan, FAKE, None, FAKE, 64, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
     assert pgq.pgq_export_model(arr, 3, plan, FAKE, None, None, 0, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
     plan[0].kind = 5  # bits 5 without matching qparams
     assert pgq.pgq_export_model(arr, 3, plan, FAKE, None, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM
