@@ -1,6 +1,6 @@
 """Throughput of the per-row weight quantizer on one MI355X.
 
-One step = one whole-model export of the 9-layer d=512 GPT weight set (21,767,168 fp32
+Default step (--mode export) = one whole-model export of the 9-layer d=512 GPT weight set (21,767,168 fp32
 parameters in 64 tensors): int6 per-row codes with the clip at the 99.99th percentile of
 |w| per row, int8 absmax for tok_emb.weight, fp16 passthrough for the 18 vectors, fp16
 row scales and the fp32 dequantized weights.  That is every step of the path in one
@@ -8,7 +8,9 @@ grouped launch (load, clip, scale, round, clamp, dequant, export dispatch).
 
 Inputs are seeded synthetic N(0, 0.02^2) weights, resident in HBM before timing.  Several
 independent copies of the inputs and outputs are used in rotation, so that no step finds
-its data in the 256 MiB Infinity Cache.  Prints one JSON line.
+its data in the 256 MiB Infinity Cache.  Prints one JSON line.  --mode selects the other
+workloads of the path (AWQ export, a 128-matrix batch, a percentile-select stress set, the STE
+forward + backward step, and a whole SQWA run), each reported the same way.
 """
 from __future__ import annotations
 
@@ -22,6 +24,10 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
 
 METRIC = "quantizer GB/s (bytes in+out) and % of MI355X HBM peak, int6 per-row"
 HBM_PEAK_GBS = 8000.0
@@ -80,11 +86,148 @@ def cpu_baseline(tensors, min_seconds: float = 10.0, max_passes: int = 4) -> dic
                       f"({el:.1f} s, single thread)"}
 
 
+class Workload:
+    """One bench workload: `step(i)` enqueues one step on input set i % copies."""
+
+    def __init__(self, name, desc, nbytes, rows, step, statuses, config, kernel):
+        self.name, self.desc, self.nbytes, self.rows = name, desc, nbytes, rows
+        self.step, self.statuses, self.config, self.kernel = step, statuses, config, kernel
+
+
+def _dev(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _bf16_dev(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def workload_export(copies, torch, ops):
+    tensors = synth.config2()
+    ab = algorithmic_bytes(tensors, want_dq=True)
+    sets = []
+    for _ in range(copies):
+        ex = ops.Exporter([ops.ExportTensor(t.name, _dev(t.data, torch)) for t in tensors], want_dq=True)
+        ex.run()                                  # uploads the descriptor table once
+        sets.append(ex)
+    cfg = {"workload": "whole-model export of the 9-layer d=512 GPT weight set: int6 per-row codes with "
+                       "99.99th-percentile clip, int8 tok_emb.weight, fp16 passthrough vectors, fp16 row "
+                       "scales, fp32 dequantized weights",
+           "tensors": len(tensors), "params": int(sum(t.numel for t in tensors))}
+    return Workload("export", cfg["workload"], ab["total"], ab["rows"], lambda i: sets[i % len(sets)].run(),
+                    lambda: [int(s.status.item()) for s in sets], cfg, "pgq_table_kernel<0, 5u>"), tensors
+
+
+def workload_awq(copies, torch, ops):
+    tensors = synth.config4()
+    pol = ops.make_policy(q_default=(6, 1, 1))
+    nbytes = rows = 0
+    for t in tensors:
+        r, c = t.shape
+        nbytes += 9 * t.numel + 2 * r
+        rows += r
+        if t.awq_s is not None:
+            nbytes += 4 * c + 2 * c               # activation scales in, fp16 multipliers out
+    sets = []
+    for _ in range(copies):
+        ex = ops.Exporter([ops.ExportTensor(t.name, _dev(t.data, torch), None if t.awq_s is None else _dev(t.awq_s, torch))
+                           for t in tensors], pol, want_dq=True)
+        ex.run()
+        sets.append(ex)
+    cfg = {"workload": "mixed-bit AWQ export of the 12-layer d=512 vocab-1792 GPT weight set: int6 per-row "
+                       "absmax on w * fp16(sqrt(s_j)), int8 tok_emb/lm_head, fp16 scales and multipliers, fp32 "
+                       "dequant", "tensors": len(tensors), "params": int(sum(t.numel for t in tensors))}
+    return Workload("awq", cfg["workload"], nbytes, rows, lambda i: sets[i % len(sets)].run(),
+                    lambda: [int(s.status.item()) for s in sets], cfg, "pgq_table_kernel<0, 13u>"), None
+
+
+def workload_batch(copies, torch, ops):
+    mats = synth.config1_batch(128)
+    pol = ops.make_policy(int8_patterns=(), passthrough_below=0, q_default=(6, 1, 1))
+    sets = []
+    for _ in range(max(2, copies // 3)):
+        ex = ops.Exporter([ops.ExportTensor(m.name, _dev(m.data, torch)) for m in mats], pol, want_dq=True)
+        ex.run()
+        sets.append(ex)
+    nbytes = 128 * (1536 * 512 * 9 + 1536 * 2)
+    cfg = {"workload": "128 independent 1536x512 fp32 matrices, int6 per-row absmax, codes + fp16 scales + fp32 "
+                       "dequant, one grouped launch", "tensors": 128, "params": 128 * 1536 * 512}
+    return Workload("batch", cfg["workload"], nbytes, 128 * 1536, lambda i: sets[i % len(sets)].run(),
+                    lambda: [int(s.status.item()) for s in sets], cfg, "pgq_table_kernel<0, 5u>"), None
+
+
+def workload_select(copies, torch, ops):
+    tensors = synth.stress_s1()
+    ab = algorithmic_bytes(tensors, want_dq=True)
+    pol = ops.make_policy(q_default=(6, 99, 100))
+    sets = []
+    for _ in range(copies):
+        ex = ops.Exporter([ops.ExportTensor(t.name, _dev(t.data, torch)) for t in tensors], pol, want_dq=True)
+        ex.run()
+        sets.append(ex)
+    cfg = {"workload": "export of heavy-tailed (0.02 * Student-t(3)) 9-layer d=512 weights with the clip at the "
+                       "99th percentile per row (exact select), int8 tok_emb, fp16 vectors, fp32 dequant",
+           "tensors": len(tensors), "params": int(sum(t.numel for t in tensors))}
+    return Workload("select", cfg["workload"], ab["total"], ab["rows"], lambda i: sets[i % len(sets)].run(),
+                    lambda: [int(s.status.item()) for s in sets], cfg, "pgq_table_kernel<0, 21u>"), None
+
+
+def workload_fakequant(copies, torch, ops, pgq):
+    ws = synth.config3_weights()
+    nbytes = rows = 0
+    for t in ws:
+        r, c = t.shape
+        nbytes += 8 * t.numel + r * ((c + 7) // 8) + 2 * r
+        rows += r
+    sets = []
+    for k in range(copies):
+        fq = ops.FakeQuant([_bf16_dev(t.data, torch) for t in ws])
+        grads = [_bf16_dev(g.data, torch) for g in synth.config3_grads(k)]
+        fq.run(pgq.PGQ_FQ_FWD_BWD, grads)
+        sets.append((fq, grads))
+    cfg = {"workload": "STE fake-quant forward + backward of the 11-layer d=528 model (unified QKV 1584x528, Wo "
+                       "528x528, MLP 1584x528 / 528x1584, bf16), int6 absmax: bf16 dequant, fp16 scales, mask bits, "
+                       "masked bf16 gradients; a fresh gradient set per step in rotation",
+           "tensors": len(ws), "params": int(sum(t.numel for t in ws))}
+    return Workload("fakequant", cfg["workload"], nbytes, rows,
+                    lambda i: sets[i % len(sets)][0].run(pgq.PGQ_FQ_FWD_BWD, sets[i % len(sets)][1]),
+                    lambda: [int(s[0].status.item()) for s in sets], cfg, "pgq_table_kernel<2, 2u>"), None
+
+
+def workload_sqwa(copies, torch, ops):
+    base = synth.config5_base()
+    snaps = [[_dev(t.data, torch) for t in synth.config5_snapshot(k, base)] for k in range(1, 17)]
+    sq = ops.Sqwa([ops.ExportTensor(t.name, s) for t, s in zip(base, snaps[0])], ops.make_policy(int8_patterns=()))
+    for k in range(1, 17):
+        sq.accumulate(snaps[k - 1], k)
+    ex = sq.exporter(want_dq=False)
+    ex.run()
+    numel = sum(t.numel for t in base)
+    nvec = sum(t.numel for t in base if t.numel < 65536)
+    rows = sum(t.shape[0] for t in base if t.numel >= 65536)
+    nbytes = 8 * numel + 15 * 12 * numel + (4 * numel + (numel - nvec) + 2 * rows + 2 * nvec)
+
+    def step(i):
+        for k in range(1, 17):
+            sq.accumulate(snaps[k - 1], k)
+        ex.run()
+
+    cfg = {"workload": "SQWA over 16 snapshots of the 9-layer d=512 weight set (snapshot k = base + N(0, "
+                       "(0.002k)^2)): int6 99.99th-percentile QDQ of every matrix, fp16 round trip of vectors, "
+                       "fp32 running mean, then int6 codes + scales of the mean; 17 launches per step",
+           "tensors": len(base), "params": int(numel), "snapshots": 16}
+    return Workload("sqwa", cfg["workload"], nbytes, 17 * rows, step,
+                    lambda: [int(sq.status.item()), int(ex.status.item())], cfg, "pgq_table_kernel<1, 5u>"), None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 1000; 50 for --mode sqwa)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 50; 3 for --mode sqwa)")
+    ap.add_argument("--mode", default="export", choices=["export", "awq", "batch", "select", "fakequant", "sqwa"],
+                    help="export (default): the 9-layer whole-model export; the others time the remaining "
+                         "rows of the path")
     ap.add_argument("--copies", type=int, default=6, help="input/output sets used in rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="N",
@@ -95,82 +238,96 @@ def main() -> int:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer is "
               f"row-parallel within a GPU and this build runs no collectives)", file=sys.stderr)
         return 2
+    steps = args.steps if args.steps is not None else (50 if args.mode == "sqwa" else 1000)
+    warmup = args.warmup if args.warmup is not None else (3 if args.mode == "sqwa" else 50)
 
-    import numpy as np
     import torch
 
-    import synth
     from int6_weight_export_amd import ops, pgq
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    tensors = synth.config2()
-    ab = algorithmic_bytes(tensors, want_dq=True)
-
-    sets = []
-    for c in range(args.copies):
-        dts = [ops.ExportTensor(t.name, torch.from_numpy(t.data).to("cuda")) for t in tensors]
-        ex = ops.Exporter(dts, want_dq=True)
-        ex.run()                                  # uploads the descriptor table once
-        sets.append(ex)
+    make = {"export": workload_export, "awq": workload_awq, "batch": workload_batch, "select": workload_select,
+            "sqwa": workload_sqwa}
+    if args.mode == "fakequant":
+        wl, tensors = workload_fakequant(args.copies, torch, ops, pgq)
+    else:
+        wl, tensors = make[args.mode](args.copies, torch, ops)
     torch.cuda.synchronize()
-    for i in range(args.warmup):
-        sets[i % len(sets)].run()
+    for i in range(warmup):
+        wl.step(i)
     torch.cuda.synchronize()
 
-    # Each launch records its own start / stop events from its dispatch (pgq_time_next_launch),
-    # so the pair times the kernel alone, on the stream it runs on, with no extra packets.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Every launch records its own start / stop events from its dispatch (pgq_time_next_launch),
+    # so a pair times one kernel alone, on the stream it runs on, with no extra packets.
+    launches = 17 if args.mode == "sqwa" else 1
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps * launches)]
     for a, b in ev:                              # create the underlying HIP events
         a.record()
         b.record()
     handles = [(ctypes.c_void_p(a.cuda_event), ctypes.c_void_p(b.cuda_event)) for a, b in ev]
+    timed_step = wl.step
+    if launches > 1:
+        it = iter(handles)
+        orig = ops.Sqwa.accumulate, ops.Exporter.run
+
+        def acc(self, *a, **k):
+            pgq.pgq_time_next_launch(*next(it))
+            return orig[0](self, *a, **k)
+
+        def run(self, *a, **k):
+            pgq.pgq_time_next_launch(*next(it))
+            return orig[1](self, *a, **k)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        pgq.pgq_time_next_launch(*handles[i])
-        sets[i % len(sets)].run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    status = [int(s.status.item()) for s in sets]
+    if launches > 1:
+        ops.Sqwa.accumulate, ops.Exporter.run = acc, run
+        t0 = time.perf_counter()
+        for i in range(steps):
+            timed_step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ops.Sqwa.accumulate, ops.Exporter.run = orig
+    else:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            pgq.pgq_time_next_launch(*handles[i])
+            timed_step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    status = wl.statuses()
     assert all(x == 0 for x in status), status
 
-    ms_per_step = wall / args.steps * 1e3
-    value = ab["total"] / (wall / args.steps) / 1e9
-    k_avg_s = float(np.mean(kern_ms)) / 1e3
-    achieved = ab["total"] / k_avg_s / 1e9
+    ms_per_step = wall / steps * 1e3
+    value = wl.nbytes / (wall / steps) / 1e9
+    k_step_s = float(kern_ms.sum()) / steps / 1e3       # kernel time per step
+    achieved = wl.nbytes / k_step_s / 1e9
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if args.mode == "export" and os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha256") == kernel_source_hash():
             traffic = tr.get("hbm_bytes_per_launch")
 
+    config = dict(wl.config)
+    config.update({"bytes_per_step": wl.nbytes, "rows_per_step": wl.rows, "input_copies_in_rotation":
+                   (1 if args.mode == "sqwa" else args.copies if args.mode != "batch" else max(2, args.copies // 3))})
     line = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if args.mode == "fakequant" else "f32",
         "data": "synthetic",
-        "config": {
-            "workload": "whole-model export of the 9-layer d=512 GPT weight set: int6 per-row codes with "
-                        "99.99th-percentile clip, int8 tok_emb.weight, fp16 passthrough vectors, fp16 row "
-                        "scales, fp32 dequantized weights",
-            "tensors": len(tensors),
-            "params": int(sum(t.numel for t in tensors)),
-            "bytes_per_step": ab["total"],
-            "rows_per_step": ab["rows"],
-            "input_copies_in_rotation": args.copies,
-        },
+        "config": config,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -179,13 +336,14 @@ def main() -> int:
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
         },
+        "kernel": wl.kernel,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "kernel_us_avg": round(k_avg_s * 1e6, 3),
-        "kernel_us_p10_p90": [round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
-                              round(float(np.percentile(kern_ms, 90)) * 1e3, 3)],
-        "rows_per_s": round(ab["rows"] / (wall / args.steps), 1),
+        "kernel_us_per_step": round(k_step_s * 1e6, 3),
+        "kernel_us_p10_p90_per_launch": [round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+                                         round(float(np.percentile(kern_ms, 90)) * 1e3, 3)],
+        "rows_per_s": round(wl.rows / (wall / steps), 1),
     }
-    if not args.no_cpu_baseline:
+    if args.mode == "export" and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(tensors)
     if args.copy_calibration:
         n = (256 << 20) // 4

@@ -375,7 +375,6 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
                                           const float (&a)[VEC], bool has_awq, const RowCtx& rc,
                                           bool valid, int lane)
 {
-    const uint32_t c = cu + (uint32_t)lane;
     const uint32_t eu = cu * VEC;                 // uniform element offset of the chunk group
     const uint32_t e = (uint32_t)lane * VEC;      // lane's element offset within it
     float r[VEC];
@@ -472,15 +471,46 @@ __device__ __forceinline__ void load_awq(const GLB float* s_row, GLB uint16_t* a
     if (a_out) store_u16<VEC>(a_out + cu * VEC, (uint32_t)lane * VEC, h);
 }
 
+// Multipliers of lane l's columns in chunk group cu from the workgroup's LDS table (1 past the row)
+template <int VEC>
+__device__ __forceinline__ void lds_awq(const float* awq_lds, uint32_t cu, int lane, int nchunk, float (&a)[VEC])
+{
+    const uint32_t c = cu + (uint32_t)lane;
+    if ((int)c < nchunk) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) a[v] = awq_lds[c * VEC + v];
+    } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) a[v] = 1.0f;
+    }
+}
+
+// All threads of the workgroup: a_j = fp16(sqrt(s_j)) for the tensor's columns into LDS; the
+// workgroup holding row 0 also writes the fp16 multipliers out.
+__device__ __forceinline__ void fill_awq_lds(const Desc& d, bool write_out, float* awq_lds, uint32_t& st)
+{
+    const GLB float* s = gp(d.awq_s);
+    GLB uint16_t* out = (write_out && d.awq_out) ? gp(d.awq_out) : nullptr;
+    for (int j = threadIdx.x; j < (int)d.cols; j += kBlock) {
+        const float v = s[j];
+        if (!(v > 0.0f) || !(v <= 3.402823466e38f)) st |= PGQ_DEV_BAD_AWQ;
+        const uint16_t h = f2h(__builtin_sqrtf(v));          // correctly rounded sqrt, then fp16
+        awq_lds[j] = h2f(h);
+        if (out) out[j] = h;
+    }
+}
+
 // ---- a group of R consecutive rows of one tensor (integer kinds) ------------------------------
 // The register tile holds NCHT chunks per lane.  A row needing NCHT / R chunks or fewer is
 // processed R rows at a time: every row's loads are issued before the first reduction, so a
 // wave keeps R rows in flight.  Rows longer than the tile (R = 1 only) stream in pieces.
 // EXACT: NCH is exactly ceil(chunks / 64) for this tensor, so chunks 0 .. NCH-2 are full and
 // only the last needs a per-lane bound; otherwise NCH is the tile share and chunks are guarded.
+// awq_lds: the tensor's AWQ multipliers a_j, computed once per workgroup into LDS (every
+// tensor with AWQ whose rows fit the register tile); longer rows compute them per chunk.
 template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R, int NCH, bool EXACT>
 __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
-                                           const KArgs& ka, uint32_t& st)
+                                           const float* awq_lds, const KArgs& ka, uint32_t& st)
 {
     constexpr int NCHT = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);   // register tile, chunks per lane
     static_assert(NCH * R <= NCHT, "the group fits the register tile");
@@ -502,7 +532,6 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
     if (R > 1 || !LONG || nchunk <= 64 * NCH) {
         static_assert(!EXACT || !LONG, "exact-width groups never stream");
         float x[R][NCH][VEC];
-        float a[AWQ ? NCH : 1][VEC];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (r < nrows) {
@@ -523,21 +552,16 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         }
         if constexpr (AWQ) {
             if (has_awq) {
-                // the column multipliers are the same for every row of the group
+                // the column multipliers are the same for every row: read them from LDS
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
                     if (EXACT || 64 * i < nchunk) {
-                        const uint32_t c = (uint32_t)(lane + 64 * i);
-                        if ((EXACT && i < NCH - 1) || (int)c < nchunk) {
-                            load_awq<VEC>(s_row, a_out, 64u * i, lane, a[i], st);
-                        } else {
-#pragma unroll
-                            for (int v = 0; v < VEC; ++v) a[i][v] = 1.0f;
-                        }
+                        float a[VEC];
+                        lds_awq<VEC>(awq_lds, 64u * i, lane, nchunk, a);
 #pragma unroll
                         for (int r = 0; r < R; ++r)
 #pragma unroll
-                            for (int v = 0; v < VEC; ++v) x[r][i][v] = x[r][i][v] * a[i][v];
+                            for (int v = 0; v < VEC; ++v) x[r][i][v] = x[r][i][v] * a[v];
                     }
                 }
             }
@@ -577,7 +601,10 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 for (int i = 0; i < NCH; ++i) {
                     if (EXACT || 64 * i < nchunk) {
                         const uint32_t c = (uint32_t)(lane + 64 * i);
-                        const float (&ai)[VEC] = a[AWQ ? i : 0];
+                        float ai[VEC];
+                        if constexpr (AWQ) {
+                            if (has_awq) lds_awq<VEC>(awq_lds, 64u * i, lane, nchunk, ai);
+                        }
                         const bool ok = (EXACT && i < NCH - 1) || (int)c < nchunk;
                         chunk_out<MODE, AWQ, VEC>(ro, 64u * i, x[r][i], ai, has_awq, rc, ok, lane);
                         __builtin_amdgcn_sched_barrier(0);
@@ -653,24 +680,24 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
 // exact chunk count (d.nch) and group size (d.rgroup); the element-wise path splits the tile.
 template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R, int NCH>
 __device__ __forceinline__ void rows_exact(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
-                                           const KArgs& ka, uint32_t& st)
+                                           const float* awq_lds, const KArgs& ka, uint32_t& st)
 {
-    rows_quant<MODE, AWQ, SEL, false, IN, VEC, R, NCH, true>(d, row0, nrows, lane, hist, ka, st);
+    rows_quant<MODE, AWQ, SEL, false, IN, VEC, R, NCH, true>(d, row0, nrows, lane, hist, awq_lds, ka, st);
 }
 
 template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC>
 __device__ __forceinline__ void rows_quant_r(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
-                                             const KArgs& ka, uint32_t& st)
+                                             const float* awq_lds, const KArgs& ka, uint32_t& st)
 {
     constexpr int NCHT = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);
     if constexpr (VEC == 1) {
         switch (d.rgroup) {
-        case 8: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 8, NCHT / 8, false>(d, row0, nrows, lane, hist, ka, st); break;
-        case 4: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 4, NCHT / 4, false>(d, row0, nrows, lane, hist, ka, st); break;
-        case 2: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 2, NCHT / 2, false>(d, row0, nrows, lane, hist, ka, st); break;
+        case 8: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 8, NCHT / 8, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
+        case 4: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 4, NCHT / 4, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
+        case 2: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 2, NCHT / 2, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
         default:
             for (int r = 0; r < nrows; ++r)
-                rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, ka, st);
+                rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, awq_lds, ka, st);
             break;
         }
         return;
@@ -680,22 +707,22 @@ __device__ __forceinline__ void rows_quant_r(const Desc& d, int64_t row0, int nr
         if (d.nch == 0) {            // longer than the register tile: stream row by row
             if constexpr (LONG) {
                 for (int r = 0; r < nrows; ++r)
-                    rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, ka, st);
+                    rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, awq_lds, ka, st);
             }
             return;
         }
         if constexpr (NCHT == 8) {
             switch (key) {
-            case 8 * 16 + 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 8, 1>(d, row0, nrows, lane, hist, ka, st); return;
-            case 4 * 16 + 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 4, 2>(d, row0, nrows, lane, hist, ka, st); return;
-            case 2 * 16 + 3: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 3>(d, row0, nrows, lane, hist, ka, st); return;
-            case 2 * 16 + 4: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 4>(d, row0, nrows, lane, hist, ka, st); return;
+            case 8 * 16 + 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 8, 1>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
+            case 4 * 16 + 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 4, 2>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
+            case 2 * 16 + 3: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 3>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
+            case 2 * 16 + 4: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 4>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
             default: break;
             }
         } else {
             switch (key) {
-            case 4 * 16 + 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 4, 1>(d, row0, nrows, lane, hist, ka, st); return;
-            case 2 * 16 + 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 2>(d, row0, nrows, lane, hist, ka, st); return;
+            case 4 * 16 + 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 4, 1>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
+            case 2 * 16 + 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 2>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
             default: break;
             }
         }
@@ -703,17 +730,17 @@ __device__ __forceinline__ void rows_quant_r(const Desc& d, int64_t row0, int nr
         for (int r = 0; r < nrows; ++r) {
             const int64_t row = row0 + r;
             switch (d.nch) {
-            case 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 1>(d, row, 1, lane, hist, ka, st); break;
-            case 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 2>(d, row, 1, lane, hist, ka, st); break;
-            case 3: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 3>(d, row, 1, lane, hist, ka, st); break;
-            case 4: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 4>(d, row, 1, lane, hist, ka, st); break;
+            case 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 1>(d, row, 1, lane, hist, awq_lds, ka, st); break;
+            case 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 2>(d, row, 1, lane, hist, awq_lds, ka, st); break;
+            case 3: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 3>(d, row, 1, lane, hist, awq_lds, ka, st); break;
+            case 4: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 4>(d, row, 1, lane, hist, awq_lds, ka, st); break;
             default:
                 if constexpr (NCHT == 8) {
                     switch (d.nch) {
-                    case 5: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 5>(d, row, 1, lane, hist, ka, st); break;
-                    case 6: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 6>(d, row, 1, lane, hist, ka, st); break;
-                    case 7: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 7>(d, row, 1, lane, hist, ka, st); break;
-                    default: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 8>(d, row, 1, lane, hist, ka, st); break;
+                    case 5: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 5>(d, row, 1, lane, hist, awq_lds, ka, st); break;
+                    case 6: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 6>(d, row, 1, lane, hist, awq_lds, ka, st); break;
+                    case 7: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 7>(d, row, 1, lane, hist, awq_lds, ka, st); break;
+                    default: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 8>(d, row, 1, lane, hist, awq_lds, ka, st); break;
                     }
                 }
                 break;
@@ -796,7 +823,7 @@ __device__ __forceinline__ void row_fq_bwd(const Desc& d, int64_t row, int lane)
 
 template <int MODE, uint32_t F>
 __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nrows, int lane, uint32_t* hist,
-                                              const KArgs& ka, uint32_t& st)
+                                              const float* awq_lds, const KArgs& ka, uint32_t& st)
 {
     constexpr bool AWQ = (F & F_AWQ) != 0;
     constexpr bool SEL = (F & F_SEL) != 0;
@@ -810,9 +837,9 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nr
         }
     } else if constexpr (MODE == MODE_FQ) {
         if constexpr (SCALAR) {
-            if (!vec) { rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 1>(d, row, nrows, lane, hist, ka, st); return; }
+            if (!vec) { rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 1>(d, row, nrows, lane, hist, awq_lds, ka, st); return; }
         }
-        rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 8>(d, row, nrows, lane, hist, ka, st);
+        rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 8>(d, row, nrows, lane, hist, awq_lds, ka, st);
     } else {
         if constexpr ((F & F_PASS) != 0) {
             if (d.kind == KIND_F16) {
@@ -841,17 +868,17 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nr
         if constexpr ((F & F_F32) != 0) {
             if (d.in_dtype == IN_F32) {
                 if constexpr (SCALAR) {
-                    if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 1>(d, row, nrows, lane, hist, ka, st); return; }
+                    if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 1>(d, row, nrows, lane, hist, awq_lds, ka, st); return; }
                 }
-                rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 4>(d, row, nrows, lane, hist, ka, st);
+                rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 4>(d, row, nrows, lane, hist, awq_lds, ka, st);
                 return;
             }
         }
         if constexpr ((F & F_BF16) != 0) {
             if constexpr (SCALAR) {
-                if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 1>(d, row, nrows, lane, hist, ka, st); return; }
+                if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 1>(d, row, nrows, lane, hist, awq_lds, ka, st); return; }
             }
-            rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 8>(d, row, nrows, lane, hist, ka, st);
+            rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 8>(d, row, nrows, lane, hist, awq_lds, ka, st);
         }
     }
 }
@@ -860,15 +887,32 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nr
 // groups interleaved over the four waves.
 template <int MODE, uint32_t F>
 __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, int lane, uint32_t* hist,
-                                        const KArgs& ka, uint32_t& st)
+                                        float* awq_lds, const KArgs& ka, uint32_t& st)
 {
+    // AWQ multipliers for the whole tile, once (rows that fit the register tile read them from
+    // LDS).  The condition is uniform over the workgroup, so every wave reaches the barriers.
+    const float* lds = nullptr;
+    if constexpr ((F & F_AWQ) != 0) {
+        if (d.awq_s && d.kind != KIND_F16 && d.nch > 0) {
+            __syncthreads();                    // readers of the previous tile's table are done
+            fill_awq_lds(d, row0 == 0, awq_lds, st);
+            __syncthreads();
+            lds = awq_lds;
+        } else if (d.awq_s && d.kind != KIND_F16 && d.rgroup > 0 && (d.flags & DF_VEC) == 0 &&
+                   d.cols <= kRegCols_Scalar) {
+            __syncthreads();
+            fill_awq_lds(d, row0 == 0, awq_lds, st);
+            __syncthreads();
+            lds = awq_lds;
+        }
+    }
     const int R = d.rgroup;
     const int groups = d.tile_rows / (kWaves * R);
     for (int g = 0; g < groups; ++g) {
         const int64_t first = row0 + ((int64_t)g * kWaves + wave) * R;
         if (first < d.rows) {
             const int nrows = (int)min((int64_t)R, d.rows - first);
-            dispatch_rows<MODE, F>(d, first, nrows, lane, hist, ka, st);
+            dispatch_rows<MODE, F>(d, first, nrows, lane, hist, lds, ka, st);
         }
     }
 }
@@ -902,6 +946,7 @@ __global__ void __launch_bounds__(kBlock) pgq_table_kernel(const TableHeader* __
                                                           const uint32_t* __restrict__ tile_desc, KArgs ka)
 {
     __shared__ uint32_t hist_all[kWaves][256];
+    __shared__ float awq_lds[(F & F_AWQ) ? kRegCols_F32 : 1];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     uint32_t* hist = hist_all[wave];
@@ -922,7 +967,7 @@ __global__ void __launch_bounds__(kBlock) pgq_table_kernel(const TableHeader* __
         const uint32_t ndi = next < ka.n_tiles ? tile_desc[next] : 0;
         const uint32_t first = tile_start[di];
         const Desc d = fetch_desc<MODE, F>(table + di);
-        do_tile<MODE, F>(d, (int64_t)(tile - first) * d.tile_rows, wave, lane, hist, ka, st);
+        do_tile<MODE, F>(d, (int64_t)(tile - first) * d.tile_rows, wave, lane, hist, awq_lds, ka, st);
         tile = next;
         di = ndi;
     }
@@ -935,12 +980,13 @@ template <int MODE, uint32_t F>
 __global__ void __launch_bounds__(kBlock) pgq_single_kernel(const Desc d, KArgs ka)
 {
     __shared__ uint32_t hist_all[kWaves][256];
+    __shared__ float awq_lds[(F & F_AWQ) ? kRegCols_F32 : 1];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     uint32_t* hist = hist_all[wave];
     uint32_t st = 0;
     for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x)
-        do_tile<MODE, F>(d, (int64_t)tile * d.tile_rows, wave, lane, hist, ka, st);
+        do_tile<MODE, F>(d, (int64_t)tile * d.tile_rows, wave, lane, hist, awq_lds, ka, st);
     st = wave_or(st);
     if (st && lane == 0 && ka.status) atomicOr(ka.status, st);
 }

@@ -117,18 +117,22 @@ class FakeQuant:
         return arr
 
     def run(self, mode: int, grads: Optional[Sequence[torch.Tensor]] = None, reuse_table: bool = True):
-        arr = self._descs(grads)
+        """Enqueue one grouped launch.  The descriptor array and the workspace holding its
+        uploaded table are kept per (mode, gradient buffers), so repeated steps over the same
+        buffers only re-enqueue the kernel."""
         n = len(self.weights)
         key = (mode, tuple(0 if grads is None else g.data_ptr() for g in (grads or [])))
-        need = ctypes.c_size_t(0)
-        pgq.check(pgq.pgq_fakequant_workspace(arr, n, ctypes.byref(need)), "pgq_fakequant_workspace")
-        ws = self._tables.get(key)
+        cached = self._tables.get(key)
         flags = 0
-        if ws is not None and reuse_table:
+        if cached is not None and reuse_table:
+            arr, ws = cached
             flags = pgq.PGQ_TABLE_RESIDENT
         else:
+            arr = self._descs(grads)
+            need = ctypes.c_size_t(0)
+            pgq.check(pgq.pgq_fakequant_workspace(arr, n, ctypes.byref(need)), "pgq_fakequant_workspace")
             ws = torch.empty(max(need.value, 64), dtype=torch.uint8, device=self.weights[0].device)
-            self._tables[key] = ws
+            self._tables[key] = (arr, ws)
         rc = pgq.pgq_fakequant_fwd_bwd(mode, arr, n, self.qp, _p(ws), ws.numel(), flags, _p(self.status), _stream())
         pgq.check(rc, "pgq_fakequant_fwd_bwd")
 
@@ -235,19 +239,23 @@ class Sqwa:
                                       ctypes.byref(wb)), "pgq_export_plan")
         self.workspace_bytes = max(wb.value, 64)
         self.status = new_status(dev)
-        self._tables: Dict[tuple, torch.Tensor] = {}
+        self._tables: Dict[tuple, tuple] = {}
 
     def accumulate(self, snapshot: Sequence[torch.Tensor], k: int, reuse_table: bool = True):
-        tensors = [ExportTensor(t.name, w, t.awq_s) for t, w in zip(self.exporter_template, snapshot)]
-        arr, keep = _tensor_in_array(tensors)
+        """Fold snapshot k (1-based) into the means.  The tensor array and the workspace with
+        its uploaded table are kept per snapshot buffer set (k is a kernel argument, not part
+        of the table), so repeated runs over resident snapshots only re-enqueue the kernel."""
         key = tuple(w.data_ptr() for w in snapshot)
-        ws = self._tables.get(key)
+        cached = self._tables.get(key)
         flags = 0
-        if ws is not None and reuse_table:
+        if cached is not None and reuse_table:
+            arr, keep, ws = cached
             flags = pgq.PGQ_TABLE_RESIDENT
         else:
+            tensors = [ExportTensor(t.name, w, t.awq_s) for t, w in zip(self.exporter_template, snapshot)]
+            arr, keep = _tensor_in_array(tensors)
             ws = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.means[0].device)
-            self._tables[key] = ws
+            self._tables[key] = (arr, keep, ws)
         rc = pgq.pgq_sqwa_accumulate(arr, self.n, self.plan, self.mean_ptrs, k, _p(ws), ws.numel(), flags,
                                      _p(self.status), _stream())
         pgq.check(rc, "pgq_sqwa_accumulate")
