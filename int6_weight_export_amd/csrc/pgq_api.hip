@@ -40,7 +40,7 @@ int groups_per_wave()
 // Upper bound on the rows a wavefront processes together.
 int max_rgroup()
 {
-    static const int v = env_int("PGQ_MAX_RGROUP", 1, 1, 8);
+    static const int v = env_int("PGQ_MAX_RGROUP", 0, 0, 8);   // 0: per-mode default
     return v;
 }
 
@@ -195,7 +195,10 @@ void set_grouping(Desc& d, int mode)
             if (vec) d.nch = (int32_t)nch;
             int p2 = 1;
             while (p2 < nch) p2 <<= 1;
-            R = std::min(std::min(ncht / p2, 8), max_rgroup());
+            // measured: STE rows (bf16, two input streams) gain from two rows per wavefront,
+            // export and SQWA rows from one
+            const int cap = max_rgroup() > 0 ? max_rgroup() : (mode == MODE_FQ ? 2 : 1);
+            R = std::min(std::min(ncht / p2, 8), cap);
             int r2 = 1;
             while (r2 * 2 <= R) r2 *= 2;
             R = r2;

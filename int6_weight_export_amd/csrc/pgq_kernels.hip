@@ -222,22 +222,23 @@ template <class Each>
 __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t* hist, int lane)
 {
     if (r <= kFastRank) {
-        // iterated maximum: strip the largest distinct magnitudes until r elements are covered
-        uint32_t thr = 0x80000000u;           // consider keys < thr
-        uint32_t rem = (uint32_t)r;
+        // iterated maximum: strip the largest distinct magnitudes until r elements are covered.
+        // One pass per round: the count of the current maximum m and the largest key below it.
         uint32_t m = 0;
+        each([&](uint32_t k, bool ok) { if (ok) m = max(m, k); });
+        m = wave_max(m);
+        uint32_t rem = (uint32_t)r;
         // each round removes at least one element, so r rounds always suffice
-        for (int round = 0; round < kFastRank; ++round) {
-            m = 0;
-            each([&](uint32_t k, bool ok) { if (ok && k < thr) m = max(m, k); });
-            m = wave_max(m);
-            if (rem == 1) return m;
-            uint32_t c = 0;
-            each([&](uint32_t k, bool ok) { c += (ok && k == m) ? 1u : 0u; });
+        for (int round = 0; round < kFastRank && rem > 1; ++round) {
+            uint32_t c = 0, below = 0;
+            each([&](uint32_t k, bool ok) {
+                c += (ok && k == m) ? 1u : 0u;
+                if (ok && k < m) below = max(below, k);
+            });
             c = wave_sum(c);
             if (c >= rem) return m;
             rem -= c;
-            thr = m;
+            m = wave_max(below);
         }
         return m;
     }
@@ -367,13 +368,33 @@ __device__ __forceinline__ RowOut row_out(const Desc& d, int64_t row)
     return ro;
 }
 
+// Second input stream of a chunk, loaded together with the weights so that its latency is not
+// paid again after the row's clip is known: the running mean (SQWA, k > 1) or the upstream
+// gradient (STE forward + backward).
+template <int MODE, int VEC>
+struct Aux {
+    float m[MODE == MODE_SQWA ? VEC : 1];
+    uint16_t g[MODE == MODE_FQ ? VEC : 1];
+};
+
+template <int MODE, int VEC>
+__device__ __forceinline__ void load_aux(const RowOut& ro, uint32_t cu, int lane, const RowCtx& rc, bool valid,
+                                         Aux<MODE, VEC>& ax)
+{
+    if constexpr (MODE == MODE_SQWA) {
+        if (rc.k > 1 && valid) load_f32<VEC>(ro.mean + cu * VEC, (uint32_t)lane * VEC, ax.m);
+    } else if constexpr (MODE == MODE_FQ) {
+        if (rc.fq_mode == PGQ_FQ_FWD_BWD && valid) load_u16<VEC>(ro.grad + cu * VEC, (uint32_t)lane * VEC, ax.g);
+    }
+}
+
 // ---- outputs of one chunk: lane l owns VEC elements at (cu + l) * VEC of the row -------------
 // cu is uniform: it moves the scalar base pointers, and every lane adds the same small offset
 // lane * VEC, so all chunks of a row share one offset register.
 template <int MODE, bool AWQ, int VEC>
 __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const float (&x)[VEC],
                                           const float (&a)[VEC], bool has_awq, const RowCtx& rc,
-                                          bool valid, int lane)
+                                          bool valid, int lane, const Aux<MODE, VEC>& ax)
 {
     const uint32_t eu = cu * VEC;                 // uniform element offset of the chunk group
     const uint32_t e = (uint32_t)lane * VEC;      // lane's element offset within it
@@ -407,12 +428,11 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
             store_f32<VEC>(mp, e, dq);
         } else {
             float m[VEC];
-            load_f32<VEC>(mp, e, m);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
-                const float diff = dq[v] - m[v];
+                const float diff = dq[v] - ax.m[v];
                 const float step = diff / rc.kf;
-                m[v] = m[v] + step;
+                m[v] = ax.m[v] + step;
             }
             store_f32<VEC>(mp, e, m);
         }
@@ -446,9 +466,8 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
         if (ro.codes) store_codes<VEC>(ro.codes + eu, e, r);
         if (rc.fq_mode == PGQ_FQ_FWD_BWD) {
             uint16_t g[VEC];
-            load_u16<VEC>(ro.grad + eu, e, g);
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) g[v] = keep[v] ? g[v] : (uint16_t)0;
+            for (int v = 0; v < VEC; ++v) g[v] = keep[v] ? ax.g[v] : (uint16_t)0;
             store_u16<VEC>(ro.gout + eu, e, g);
         }
     }
@@ -532,9 +551,16 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
     if (R > 1 || !LONG || nchunk <= 64 * NCH) {
         static_assert(!EXACT || !LONG, "exact-width groups never stream");
         float x[R][NCH][VEC];
+        Aux<MODE, VEC> ax[R][NCH];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (r < nrows) {
+                const RowOut ro = row_out(d, row0 + r);
+#pragma unroll
+                for (int i = 0; i < NCH; ++i)
+                    if (EXACT || 64 * i < nchunk)
+                        load_aux<MODE, VEC>(ro, 64u * i, lane, rc, (EXACT && i < NCH - 1) || lane + 64 * i < nchunk,
+                                            ax[r][i]);
                 const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)((row0 + r) * d.ld) * esz;
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
@@ -606,7 +632,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                             if (has_awq) lds_awq<VEC>(awq_lds, 64u * i, lane, nchunk, ai);
                         }
                         const bool ok = (EXACT && i < NCH - 1) || (int)c < nchunk;
-                        chunk_out<MODE, AWQ, VEC>(ro, 64u * i, x[r][i], ai, has_awq, rc, ok, lane);
+                        chunk_out<MODE, AWQ, VEC>(ro, 64u * i, x[r][i], ai, has_awq, rc, ok, lane, ax[r][i]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -671,7 +697,9 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) { x[v] = 0.0f; a[v] = 1.0f; }
             }
-            chunk_out<MODE, AWQ, VEC>(ro, (uint32_t)base, x, a, has_awq, rc, ok, lane);
+            Aux<MODE, VEC> ax;
+            load_aux<MODE, VEC>(ro, (uint32_t)base, lane, rc, ok, ax);
+            chunk_out<MODE, AWQ, VEC>(ro, (uint32_t)base, x, a, has_awq, rc, ok, lane, ax);
         }
     }
 }
@@ -999,8 +1027,9 @@ const void* kernel_ptr(bool table)
 }
 
 // Instantiations per mode, leanest first; the last covers every feature.
-constexpr uint32_t kExportVariants[] = {F_F32 | F_PASS, F_BF16 | F_PASS, F_F32 | F_PASS | F_AWQ, F_ALL};
-constexpr uint32_t kFqVariants[] = {F_BF16, F_ALL};
+constexpr uint32_t kExportVariants[] = {F_F32 | F_PASS, F_BF16 | F_PASS, F_F32 | F_PASS | F_AWQ,
+                                        F_F32 | F_PASS | F_SEL, F_ALL};
+constexpr uint32_t kFqVariants[] = {F_BF16, F_BF16 | F_SEL, F_ALL};
 
 template <int MODE>
 const void* export_like(uint32_t v, bool table)
@@ -1009,6 +1038,7 @@ const void* export_like(uint32_t v, bool table)
     case F_F32 | F_PASS: return kernel_ptr<MODE, F_F32 | F_PASS>(table);
     case F_BF16 | F_PASS: return kernel_ptr<MODE, F_BF16 | F_PASS>(table);
     case F_F32 | F_PASS | F_AWQ: return kernel_ptr<MODE, F_F32 | F_PASS | F_AWQ>(table);
+    case F_F32 | F_PASS | F_SEL: return kernel_ptr<MODE, F_F32 | F_PASS | F_SEL>(table);
     default: return kernel_ptr<MODE, F_ALL>(table);
     }
 }
@@ -1019,7 +1049,10 @@ const void* pick(int mode, uint32_t need, bool table)
     switch (mode) {
     case MODE_EXPORT: return export_like<MODE_EXPORT>(v, table);
     case MODE_SQWA: return export_like<MODE_SQWA>(v, table);
-    case MODE_FQ: return v == F_BF16 ? kernel_ptr<MODE_FQ, F_BF16>(table) : kernel_ptr<MODE_FQ, F_ALL>(table);
+    case MODE_FQ:
+        if (v == F_BF16) return kernel_ptr<MODE_FQ, F_BF16>(table);
+        if (v == (F_BF16 | F_SEL)) return kernel_ptr<MODE_FQ, F_BF16 | F_SEL>(table);
+        return kernel_ptr<MODE_FQ, F_ALL>(table);
     case MODE_FQ_BWD: return kernel_ptr<MODE_FQ_BWD, F_ALL>(table);
     default: return nullptr;
     }
