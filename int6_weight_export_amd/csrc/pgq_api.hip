@@ -37,6 +37,14 @@ int groups_per_wave()
     return v;
 }
 
+// Row groups per wavefront in a tile of a tensor with AWQ multipliers: the workgroup computes
+// the multipliers (and their reciprocals) once per tile, so longer tiles amortise that.
+int awq_groups_per_wave()
+{
+    static const int v = env_int("PGQ_AWQ_GROUPS_PER_WAVE", 2, 1, 64);
+    return v;
+}
+
 // Upper bound on the rows a wavefront processes together.
 int max_rgroup()
 {
@@ -205,7 +213,8 @@ void set_grouping(Desc& d, int mode)
         }
     }
     d.rgroup = R;
-    d.tile_rows = kWaves * R * groups_per_wave();
+    const bool awq_tile = d.awq_s && d.kind != KIND_F16 && mode != MODE_FQ && mode != MODE_FQ_BWD;
+    d.tile_rows = kWaves * R * std::max(groups_per_wave(), awq_tile ? awq_groups_per_wave() : 1);
 }
 
 // Upper bound on the tiles of a tensor (group size 1), for sizing workspaces before the

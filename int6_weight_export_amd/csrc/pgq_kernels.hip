@@ -393,8 +393,8 @@ __device__ __forceinline__ void load_aux(const RowOut& ro, uint32_t cu, int lane
 // lane * VEC, so all chunks of a row share one offset register.
 template <int MODE, bool AWQ, int VEC>
 __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const float (&x)[VEC],
-                                          const float (&a)[VEC], bool has_awq, const RowCtx& rc,
-                                          bool valid, int lane, const Aux<MODE, VEC>& ax)
+                                          const float (&a)[VEC], const float (&ainv)[VEC], bool has_awq,
+                                          const RowCtx& rc, bool valid, int lane, const Aux<MODE, VEC>& ax)
 {
     const uint32_t eu = cu * VEC;                 // uniform element offset of the chunk group
     const uint32_t e = (uint32_t)lane * VEC;      // lane's element offset within it
@@ -405,7 +405,14 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
     for (int v = 0; v < VEC; ++v) {
         dq[v] = r[v] * rc.sf;                     // exact (<= 8 + 11 significant bits); +0 for code 0
         if constexpr (AWQ) {
-            if (has_awq) dq[v] = dq[v] / a[v];
+            // fl32(dq / a) from the correctly rounded reciprocal ainv = fl32(1/a): one product and
+            // one remainder correction (Markstein).  Exact for every numerator of <= 18 and
+            // denominator of <= 11 significant bits (no under/overflow is reachable here).
+            if (has_awq) {
+                const float q = dq[v] * ainv[v];
+                const float rem = __builtin_fmaf(-q, a[v], dq[v]);
+                dq[v] = __builtin_fmaf(rem, ainv[v], q);
+            }
         }
     }
     if constexpr (MODE == MODE_EXPORT) {
@@ -476,7 +483,7 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
 // AWQ multipliers of lane l's columns in chunk group cu (cu uniform)
 template <int VEC>
 __device__ __forceinline__ void load_awq(const GLB float* s_row, GLB uint16_t* a_out, uint32_t cu, int lane,
-                                         float (&a)[VEC], uint32_t& st)
+                                         float (&a)[VEC], float (&ainv)[VEC], uint32_t& st)
 {
     float s[VEC];
     load_f32<VEC>(s_row + cu * VEC, (uint32_t)lane * VEC, s);
@@ -486,22 +493,35 @@ __device__ __forceinline__ void load_awq(const GLB float* s_row, GLB uint16_t* a
         if (!(s[v] > 0.0f) || !(s[v] <= 3.402823466e38f)) st |= PGQ_DEV_BAD_AWQ;
         h[v] = f2h(__builtin_sqrtf(s[v]));       // correctly rounded sqrt, then fp16
         a[v] = h2f(h[v]);
+        ainv[v] = 1.0f / a[v];                    // correctly rounded divide
     }
     if (a_out) store_u16<VEC>(a_out + cu * VEC, (uint32_t)lane * VEC, h);
 }
 
-// Multipliers of lane l's columns in chunk group cu from the workgroup's LDS table (1 past the row)
+// Multipliers of lane l's columns in chunk group cu from the workgroup's LDS table.  The table
+// holds a_j in [0, kRegCols_F32) and fl32(1/a_j) in [kRegCols_F32, 2 kRegCols_F32), both padded
+// with 1.0 past the row up to the register tile's extent, so no lane needs a bound.
 template <int VEC>
-__device__ __forceinline__ void lds_awq(const float* awq_lds, uint32_t cu, int lane, int nchunk, float (&a)[VEC])
+__device__ __forceinline__ void lds_awq(const float* awq_lds, uint32_t cu, int lane, float (&a)[VEC])
 {
     const uint32_t c = cu + (uint32_t)lane;
-    if ((int)c < nchunk) {
+    if constexpr (VEC % 4 == 0) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) a[v] = awq_lds[c * VEC + v];
+        for (int v = 0; v < VEC; v += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(awq_lds + c * VEC + v);
+            a[v] = t[0]; a[v + 1] = t[1]; a[v + 2] = t[2]; a[v + 3] = t[3];
+        }
     } else {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) a[v] = 1.0f;
+        for (int v = 0; v < VEC; ++v) a[v] = awq_lds[c * VEC + v];
     }
+}
+
+// Extent of the AWQ table: the register tile's chunks cover cols rounded up to 64 * VEC, and
+// VEC divides 8 and kRegCols_F32 is a multiple of 512.
+__device__ __forceinline__ int awq_extent(int64_t cols)
+{
+    return (int)min((cols + 511) & ~(int64_t)511, (int64_t)kRegCols_F32);
 }
 
 // All threads of the workgroup: a_j = fp16(sqrt(s_j)) for the tensor's columns into LDS; the
@@ -510,12 +530,20 @@ __device__ __forceinline__ void fill_awq_lds(const Desc& d, bool write_out, floa
 {
     const GLB float* s = gp(d.awq_s);
     GLB uint16_t* out = (write_out && d.awq_out) ? gp(d.awq_out) : nullptr;
-    for (int j = threadIdx.x; j < (int)d.cols; j += kBlock) {
-        const float v = s[j];
-        if (!(v > 0.0f) || !(v <= 3.402823466e38f)) st |= PGQ_DEV_BAD_AWQ;
-        const uint16_t h = f2h(__builtin_sqrtf(v));          // correctly rounded sqrt, then fp16
-        awq_lds[j] = h2f(h);
-        if (out) out[j] = h;
+    const int cols = (int)d.cols;
+    const int ext = awq_extent(d.cols);
+    for (int j = threadIdx.x; j < ext; j += kBlock) {
+        float a = 1.0f, y = 1.0f;
+        if (j < cols) {
+            const float v = s[j];
+            if (!(v > 0.0f) || !(v <= 3.402823466e38f)) st |= PGQ_DEV_BAD_AWQ;
+            const uint16_t h = f2h(__builtin_sqrtf(v));      // correctly rounded sqrt, then fp16
+            a = h2f(h);
+            y = 1.0f / a;                                    // correctly rounded divide
+            if (out) out[j] = h;
+        }
+        awq_lds[j] = a;
+        awq_lds[kRegCols_F32 + j] = y;
     }
 }
 
@@ -583,7 +611,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 for (int i = 0; i < NCH; ++i) {
                     if (EXACT || 64 * i < nchunk) {
                         float a[VEC];
-                        lds_awq<VEC>(awq_lds, 64u * i, lane, nchunk, a);
+                        lds_awq<VEC>(awq_lds, 64u * i, lane, a);
 #pragma unroll
                         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -627,12 +655,15 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 for (int i = 0; i < NCH; ++i) {
                     if (EXACT || 64 * i < nchunk) {
                         const uint32_t c = (uint32_t)(lane + 64 * i);
-                        float ai[VEC];
+                        float ai[VEC], yi[VEC];
                         if constexpr (AWQ) {
-                            if (has_awq) lds_awq<VEC>(awq_lds, 64u * i, lane, nchunk, ai);
+                            if (has_awq) {
+                                lds_awq<VEC>(awq_lds, 64u * i, lane, ai);
+                                lds_awq<VEC>(awq_lds + kRegCols_F32, 64u * i, lane, yi);
+                            }
                         }
                         const bool ok = (EXACT && i < NCH - 1) || (int)c < nchunk;
-                        chunk_out<MODE, AWQ, VEC>(ro, 64u * i, x[r][i], ai, has_awq, rc, ok, lane, ax[r][i]);
+                        chunk_out<MODE, AWQ, VEC>(ro, 64u * i, x[r][i], ai, yi, has_awq, rc, ok, lane, ax[r][i]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -644,23 +675,24 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
         const RowOut ro = row_out(d, row);
         // cu: uniform chunk base of the piece; lane l takes chunk cu + l
-        auto load_chunk = [&](uint32_t cu, float (&x)[VEC], float (&a)[VEC], GLB uint16_t* aw) {
+        auto load_chunk = [&](uint32_t cu, float (&x)[VEC], float (&a)[VEC], float (&ainv)[VEC],
+                              GLB uint16_t* aw) {
             load_x<IN, VEC>(offset_row<IN>(wrow, cu * VEC), (uint32_t)lane * VEC, x);
             if (has_awq) {
-                load_awq<VEC>(s_row, aw, cu, lane, a, st);
+                load_awq<VEC>(s_row, aw, cu, lane, a, ainv, st);
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) x[v] = x[v] * a[v];
             } else {
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) a[v] = 1.0f;
+                for (int v = 0; v < VEC; ++v) { a[v] = 1.0f; ainv[v] = 1.0f; }
             }
         };
         uint32_t mx = 0;
         for (int base = 0; base < nchunk; base += 64) {
             const uint32_t c = (uint32_t)(base + lane);
             if ((int)c < nchunk) {
-                float x[VEC], a[VEC];
-                load_chunk((uint32_t)base, x, a, a_out);
+                float x[VEC], a[VEC], ainv[VEC];
+                load_chunk((uint32_t)base, x, a, ainv, a_out);
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[v]) & 0x7FFFFFFFu);
             }
@@ -674,8 +706,8 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                     for (int base = 0; base < nchunk; base += 64) {
                         const uint32_t c = (uint32_t)(base + lane);
                         if ((int)c < nchunk) {
-                            float x[VEC], a[VEC];
-                            load_chunk((uint32_t)base, x, a, nullptr);
+                            float x[VEC], a[VEC], ainv[VEC];
+                            load_chunk((uint32_t)base, x, a, ainv, nullptr);
 #pragma unroll
                             for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, true);
                         }
@@ -690,16 +722,16 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         for (int base = 0; base < nchunk; base += 64) {
             const uint32_t c = (uint32_t)(base + lane);
             const bool ok = (int)c < nchunk;
-            float x[VEC], a[VEC];
+            float x[VEC], a[VEC], ainv[VEC];
             if (ok) {
-                load_chunk((uint32_t)base, x, a, nullptr);
+                load_chunk((uint32_t)base, x, a, ainv, nullptr);
             } else {
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) { x[v] = 0.0f; a[v] = 1.0f; }
+                for (int v = 0; v < VEC; ++v) { x[v] = 0.0f; a[v] = 1.0f; ainv[v] = 1.0f; }
             }
             Aux<MODE, VEC> ax;
             load_aux<MODE, VEC>(ro, (uint32_t)base, lane, rc, ok, ax);
-            chunk_out<MODE, AWQ, VEC>(ro, (uint32_t)base, x, a, has_awq, rc, ok, lane, ax);
+            chunk_out<MODE, AWQ, VEC>(ro, (uint32_t)base, x, a, ainv, has_awq, rc, ok, lane, ax);
         }
     }
 }
@@ -974,7 +1006,7 @@ __global__ void __launch_bounds__(kBlock) pgq_table_kernel(const TableHeader* __
                                                           const uint32_t* __restrict__ tile_desc, KArgs ka)
 {
     __shared__ uint32_t hist_all[kWaves][256];
-    __shared__ float awq_lds[(F & F_AWQ) ? kRegCols_F32 : 1];
+    __shared__ __align__(16) float awq_lds[(F & F_AWQ) ? 2 * kRegCols_F32 : 1];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     uint32_t* hist = hist_all[wave];
@@ -1008,7 +1040,7 @@ template <int MODE, uint32_t F>
 __global__ void __launch_bounds__(kBlock) pgq_single_kernel(const Desc d, KArgs ka)
 {
     __shared__ uint32_t hist_all[kWaves][256];
-    __shared__ float awq_lds[(F & F_AWQ) ? kRegCols_F32 : 1];
+    __shared__ __align__(16) float awq_lds[(F & F_AWQ) ? 2 * kRegCols_F32 : 1];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     uint32_t* hist = hist_all[wave];
