@@ -215,6 +215,9 @@ pgq_status pgq_time_next_launch(void* start_event, void* stop_event);
 /* ------------------------------------------------------------------------------------------ */
 const char* pgq_status_str(pgq_status s);   /* static string */
 const char* pgq_version(void);              /* static string */
+/* Text of the HIP runtime error behind the calling thread's most recent PGQ_ERR_HIP ("" if     */
+/* there was none); a static string owned by the HIP runtime.                                   */
+const char* pgq_last_error(void);
 
 #ifdef __cplusplus
 }

@@ -83,9 +83,9 @@ int64_t rank_top(int64_t n, uint32_t num, uint32_t den)
 uint64_t table_hash(const void* data, size_t n, uint64_t h)
 {
     const uint8_t* p = static_cast<const uint8_t*>(data);
-    for (size_t i = 0; i + 8 <= n; i += 8) {
-        uint64_t w;
-        memcpy(&w, p + i, 8);
+    for (size_t i = 0; i < n; i += 8) {
+        uint64_t w = 0;
+        memcpy(&w, p + i, std::min<size_t>(8, n - i));
         h = (h ^ w) * 0x9E3779B97F4A7C15ull;
         h ^= h >> 29;
     }
@@ -232,10 +232,25 @@ uint64_t tiles_for(const Desc& d)
     return (uint64_t)((d.rows + d.tile_rows - 1) / d.tile_rows);
 }
 
+// The HIP error behind this thread's latest PGQ_ERR_HIP (pgq_last_error).
+thread_local hipError_t t_last_hip = hipSuccess;
+
+pgq_status hip_failed(hipError_t e)
+{
+    t_last_hip = e;
+    return PGQ_ERR_HIP;
+}
+
 // Build the table on the host, upload it (unless resident) and launch one grouped kernel.
-pgq_status run_grouped(int mode, const std::vector<Desc>& descs, void* ws, size_t ws_bytes,
+pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, size_t ws_bytes,
                        uint32_t flags, uint32_t* dev_status, int sqwa_k, int fq_mode, void* stream)
 {
+    // Longest tiles first: workgroups start in tile order, so the launch ends on the shortest
+    // tiles and its tail is short.  (The tensors' order has no other meaning to the kernel.)
+    std::vector<Desc> descs(descs_in);
+    std::stable_sort(descs.begin(), descs.end(), [](const Desc& a, const Desc& b) {
+        return (int64_t)a.tile_rows * a.cols > (int64_t)b.tile_rows * b.cols;
+    });
     const size_t n = descs.size();
     std::vector<uint32_t> start(n + 1, 0);
     uint64_t total = 0;
@@ -251,28 +266,33 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs, void* ws, size_
     if (ws_bytes < need) return PGQ_ERR_WORKSPACE;
     if (!aligned(ws, 64)) return PGQ_ERR_ALIGN;
 
-    std::vector<uint64_t> buf8((need + 7) / 8, 0);
-    uint8_t* buf = reinterpret_cast<uint8_t*>(buf8.data());
-    TableHeader* hdr = reinterpret_cast<TableHeader*>(buf);
+    // The checksum covers the descriptors and the tile prefix (the per-tile descriptor index is
+    // a function of the prefix), so a call on a resident table hashes ~n * 160 bytes and
+    // builds nothing else.
     const size_t desc_off = sizeof(TableHeader);
     const size_t start_off = desc_off + align_up((int64_t)(n * sizeof(Desc)), 64);
     const size_t tdesc_off = start_off + align_up((int64_t)((n + 1) * sizeof(uint32_t)), 64);
-    memcpy(buf + desc_off, descs.data(), n * sizeof(Desc));
-    memcpy(buf + start_off, start.data(), (n + 1) * sizeof(uint32_t));
-    uint32_t* tdesc = reinterpret_cast<uint32_t*>(buf + tdesc_off);
-    for (size_t i = 0; i < n; ++i)
-        for (uint32_t t = start[i]; t < start[i + 1]; ++t) tdesc[t] = (uint32_t)i;
-    uint64_t h = table_hash(buf + desc_off, need - desc_off, 0x243F6A8885A308D3ull ^ (uint64_t)mode);
+    uint64_t h = table_hash(descs.data(), n * sizeof(Desc), 0x243F6A8885A308D3ull ^ (uint64_t)mode);
+    h = table_hash(start.data(), (n + 1) * sizeof(uint32_t), h);
     h = table_hash(&total, 8, h);
-    hdr->magic = kTableMagic;
-    hdr->checksum = h;
-    hdr->n_desc = (uint32_t)n;
-    hdr->n_tiles = (uint32_t)total;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!(flags & PGQ_TABLE_RESIDENT)) {
+        std::vector<uint64_t> buf8((need + 7) / 8, 0);
+        uint8_t* buf = reinterpret_cast<uint8_t*>(buf8.data());
+        TableHeader* hdr = reinterpret_cast<TableHeader*>(buf);
+        memcpy(buf + desc_off, descs.data(), n * sizeof(Desc));
+        memcpy(buf + start_off, start.data(), (n + 1) * sizeof(uint32_t));
+        uint32_t* tdesc = reinterpret_cast<uint32_t*>(buf + tdesc_off);
+        for (size_t i = 0; i < n; ++i)
+            for (uint32_t t = start[i]; t < start[i + 1]; ++t) tdesc[t] = (uint32_t)i;
+        hdr->magic = kTableMagic;
+        hdr->checksum = h;
+        hdr->n_desc = (uint32_t)n;
+        hdr->n_tiles = (uint32_t)total;
         // A pageable source is staged by the runtime before this call returns.
-        if (hipMemcpyAsync(ws, buf, need, hipMemcpyHostToDevice, s) != hipSuccess) return PGQ_ERR_HIP;
+        const hipError_t e = hipMemcpyAsync(ws, buf, need, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_failed(e);
     }
     KArgs ka;
     memset(&ka, 0, sizeof(ka));
@@ -288,8 +308,8 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs, void* ws, size_
     uint32_t feats = 0;
     for (const Desc& d : descs) feats |= features_of(d);
     const uint32_t grid = grid_for(mode, feats, true, ka.n_tiles);
-    if (launch(mode, feats, ka, nullptr, grid, stream) != 0) return PGQ_ERR_HIP;
-    if (hipGetLastError() != hipSuccess) return PGQ_ERR_HIP;
+    if (const int e = launch(mode, feats, ka, nullptr, grid, stream)) return hip_failed((hipError_t)e);
+    if (const hipError_t e = hipGetLastError()) return hip_failed(e);
     return PGQ_OK;
 }
 
@@ -306,8 +326,8 @@ pgq_status run_single(int mode, const Desc& d, uint32_t* dev_status, int sqwa_k,
     ka.fq_mode = fq_mode;
     const uint32_t need = features_of(d);
     const uint32_t grid = grid_for(mode, need, false, ka.n_tiles);
-    if (launch(mode, need, ka, &d, grid, stream) != 0) return PGQ_ERR_HIP;
-    if (hipGetLastError() != hipSuccess) return PGQ_ERR_HIP;
+    if (const int e = launch(mode, need, ka, &d, grid, stream)) return hip_failed((hipError_t)e);
+    if (const hipError_t e = hipGetLastError()) return hip_failed(e);
     return PGQ_OK;
 }
 
@@ -381,6 +401,11 @@ pgq_status export_desc(const pgq_tensor_in& t, const pgq_tensor_plan& p, uint8_t
 extern "C" {
 
 const char* pgq_version(void) { return "pgq 0.1 (gfx950)"; }
+
+const char* pgq_last_error(void)
+{
+    return t_last_hip == hipSuccess ? "" : hipGetErrorString(t_last_hip);
+}
 
 pgq_status pgq_time_next_launch(void* start_event, void* stop_event)
 {

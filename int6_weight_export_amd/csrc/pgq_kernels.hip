@@ -999,8 +999,17 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
 
 // Grouped launches: descriptors come from the table in the workspace through restrict-qualified
 // pointers (read-only for the whole launch, so scalar loads).  F is the feature set compiled in.
+// Occupancy floor for the lean streaming variants, chosen so the register budget still needs
+// no scratch: 7 waves per SIMD (<= 72 VGPRs) for export rows, 5 (<= 96) for fp32 SQWA rows,
+// which also keep a running mean in flight.  Measured: ~1% faster each; a floor that forces
+// spilling (export at 8 waves, STE at 6) is slower.
 template <int MODE, uint32_t F>
-__global__ void __launch_bounds__(kBlock) pgq_table_kernel(const TableHeader* __restrict__ hdr,
+constexpr int kMinWaves = (MODE == MODE_EXPORT && (F == (F_F32 | F_PASS) || F == (F_BF16 | F_PASS))) ? 7 :
+                          (MODE == MODE_SQWA && F == (F_F32 | F_PASS)) ? 5 : 1;
+
+template <int MODE, uint32_t F>
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<MODE, F>)))
+pgq_table_kernel(const TableHeader* __restrict__ hdr,
                                                           const Desc* __restrict__ table,
                                                           const uint32_t* __restrict__ tile_start,
                                                           const uint32_t* __restrict__ tile_desc, KArgs ka)

@@ -41,7 +41,8 @@ PGQ_FQ_FWD_BWD = 3
 class PgqError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
-        super().__init__(f"{what}: {pgq_status_str(status)} (status {status})")
+        detail = f" [{pgq_last_error()}]" if status == PGQ_ERR_HIP else ""
+        super().__init__(f"{what}: {pgq_status_str(status)} (status {status}){detail}")
 
 
 class pgq_qparams(ctypes.Structure):
@@ -93,10 +94,19 @@ SIGNATURES = {
     "pgq_time_next_launch": (_I32, [_P, _P]),
     "pgq_status_str": (ctypes.c_char_p, [_I32]),
     "pgq_version": (ctypes.c_char_p, []),
+    "pgq_last_error": (ctypes.c_char_p, []),
 }
 
 
 def _load():
+    # One HIP runtime per process: PyTorch-ROCm ships its own libamdhip64 (soname
+    # libamdhip64.so.7) and loads it by file name, so if libpgq were loaded first it would pull
+    # in the system runtime and PyTorch a second copy, which then disagree about the device.
+    # Loading PyTorch first lets libpgq's dependency resolve to the runtime already mapped.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libpgq.so is not built ({LIB_PATH}); run __graft_entry__.build() or "
                           f"python -m int6_weight_export_amd.build")
@@ -149,6 +159,10 @@ def pgq_status_str(s: int) -> str:
 
 def pgq_version() -> str:
     return _lib.pgq_version().decode()
+
+
+def pgq_last_error() -> str:
+    return _lib.pgq_last_error().decode()
 
 
 def check(status: int, what: str = "pgq") -> None:

@@ -5,6 +5,7 @@ sign of zero included.  Cases: the five workloads at full size (the
 oracle checks every output, or sampled tensors where the oracle would take minutes), ragged
 and misaligned shapes, heavy-tailed and long rows, edge rows and status bits.
 """
+import os
 import sys
 
 import numpy as np
@@ -378,3 +379,20 @@ def test_empty_inputs_are_noops():
     assert rc == pgq.PGQ_OK
     fq = pgq.pgq_fakequant_fwd_bwd(pgq.PGQ_FQ_FWD, None, 0, ops.qparams(6), None, 0, 0, None, ops._stream())
     assert fq == pgq.PGQ_OK
+
+
+def test_binding_loaded_before_torch():
+    """A process that imports the binding before PyTorch still runs one HIP runtime."""
+    say("binding imported before torch (subprocess)")
+    import subprocess
+    code = ("import int6_weight_export_amd.pgq as pgq\n"
+            "import torch\n"
+            "from int6_weight_export_amd import ops\n"
+            "w = torch.randn(64, 512, device='cuda') * 0.02\n"
+            "out = ops.quantize_rows(w, bits=6)\n"
+            "torch.cuda.synchronize()\n"
+            "assert int(out['status'].item()) == 0\n"
+            "print('ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
