@@ -65,6 +65,10 @@ def load():
             lib.orc_f16_passthrough.restype = _U32
             lib.orc_sqwa_update.argtypes = [_P, _P, _I64, _I32]
             lib.orc_sqwa_update.restype = None
+            lib.orc_ema_update.argtypes = [_P, _P, _I64, ctypes.c_float, _I32]
+            lib.orc_ema_update.restype = _U32
+            lib.orc_swa_update.argtypes = [_P, _P, _I64, _I32]
+            lib.orc_swa_update.restype = _U32
             _lib = lib
     return _lib
 
@@ -172,3 +176,19 @@ def sqwa_update(mean: np.ndarray, xhat, k: int) -> np.ndarray:
     assert xhat.size == mean.size
     load().orc_sqwa_update(_ptr(mean), _ptr(xhat), mean.size, k)
     return mean
+
+
+def ema_update(e: np.ndarray, w, decay: float, init: bool = False) -> int:
+    """In-place EMA update of a contiguous float32 array e with weights w; returns the status."""
+    assert e.dtype == np.float32 and e.flags.c_contiguous
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    assert w.size == e.size
+    return int(load().orc_ema_update(_ptr(e), _ptr(w), e.size, float(np.float32(decay)), 1 if init else 0))
+
+
+def swa_update(mean: np.ndarray, w, k: int) -> int:
+    """In-place running-mean (SWA) update with checkpoint k (1-based); returns the status."""
+    assert mean.dtype == np.float32 and mean.flags.c_contiguous
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    assert w.size == mean.size
+    return int(load().orc_swa_update(_ptr(mean), _ptr(w), mean.size, k))

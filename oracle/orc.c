@@ -23,7 +23,9 @@
  *     (mixed-bit int6 AWQ export) and Mixed-bit quantization details (int8 for the
  *     named sensitive tensors).
  *   - "Discriminative TTT + SLOT-24" card (PR #1414), Novel Contributions: averaging
- *     quantize-dequantize snapshots (SQWA).
+ *     quantize-dequantize snapshots (SQWA); Weight Averaging: EMA with decay 0.997.
+ *   - "SubSixteen v2" card (PR #69), Novel Contributions and Weight Averaging: SWA over 16
+ *     checkpoints.
  * Where the pages leave the arithmetic open (rounding of the scale, tie rule, zero
  * scale, percentile rank, mask boundary, AWQ exponent) the readings are: scale =
  * fp16_rne(fp32(clip / Q)), 1.0 when that is zero; codes = clamp(rne(fp32(x / s)));
@@ -262,6 +264,45 @@ uint32_t orc_f16_passthrough(const float* x, int64_t n, uint16_t* y)
         if (!isfinite(x[j])) st |= ORC_NONFINITE;
         else if ((y[j] & 0x7FFFu) == 0x7C00u) st |= ORC_F16_OVF;
     }
+    return st;
+}
+
+/* Exponential moving average of the weights (the "EMA" weight averaging of the PR #1414 and
+ * PR #1202 cards, section Weight Averaging, decay 0.997): after a step, e = decay * e +
+ * (1 - decay) * w; the first update (init != 0) starts the average at the weights, e = w.
+ * Reading of the arithmetic (the pages give only the decay): binary32 throughout; the weight
+ * factor c = fp32(1 - decay) is formed once; then fp32(fp32(decay * e) + fp32(c * w)), two
+ * products and a sum, no fused multiply-add.  Returns NONFINITE when a weight or a new
+ * average is NaN or infinite. */
+uint32_t orc_ema_update(float* e, const float* w, int64_t n, float decay, int32_t init)
+{
+    uint32_t st = 0;
+    const float c = 1.0f - decay;
+    for (int64_t j = 0; j < n; ++j) {
+        if (init) {
+            e[j] = w[j];
+        } else {
+            float kept = decay * e[j];
+            float added = c * w[j];
+            e[j] = kept + added;
+        }
+        if (!isfinite(w[j]) || !isfinite(e[j])) st |= ORC_NONFINITE;
+    }
+    return st;
+}
+
+/* SWA (PR #69 card: "Stochastic Weight Averaging over 16 checkpoints", Weight Averaging
+ * parameters checkpoints 16, interval 200 steps): the arithmetic mean of the checkpoints
+ * handed over in order, k = 1, 2, ..., kept as a running mean with the same binary32 update
+ * as orc_sqwa_update below (there on quantize-dequantized snapshots, here on the weights). */
+void orc_sqwa_update(float* mean, const float* xhat, int64_t n, int32_t k);
+
+uint32_t orc_swa_update(float* mean, const float* w, int64_t n, int32_t k)
+{
+    uint32_t st = 0;
+    orc_sqwa_update(mean, w, n, k);
+    for (int64_t j = 0; j < n; ++j)
+        if (!isfinite(w[j]) || !isfinite(mean[j])) st |= ORC_NONFINITE;
     return st;
 }
 

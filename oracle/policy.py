@@ -117,3 +117,30 @@ def sqwa_run(snapshots, pol: Policy, k0: int = 1, means: Optional[List[np.ndarra
             lib.sqwa_update(means[i], xhat, k)
         k += 1
     return means
+
+
+def ema_run(steps, decay: float, states: Optional[List[np.ndarray]] = None):
+    """EMA over a sequence of weight sets (each a list of arrays, one per tensor).  With no
+    `states` the first set initialises the averages.  Returns (float32 states, status OR)."""
+    st = 0
+    for ws in steps:
+        init = states is None
+        if init:
+            states = [np.empty(np.asarray(w).shape, dtype=np.float32) for w in ws]
+        for e, w in zip(states, ws):
+            st |= lib.ema_update(e, np.asarray(w, dtype=np.float32), decay, init)
+    return states, st
+
+
+def swa_run(checkpoints, k0: int = 1, means: Optional[List[np.ndarray]] = None):
+    """SWA running means over checkpoints k0, k0+1, ... (each a list of arrays).
+    Returns (float32 means, status OR); `means` resumes a run."""
+    st = 0
+    k = k0
+    for ws in checkpoints:
+        if means is None:
+            means = [np.empty(np.asarray(w).shape, dtype=np.float32) for w in ws]
+        for m, w in zip(means, ws):
+            st |= lib.swa_update(m, np.asarray(w, dtype=np.float32), k)
+        k += 1
+    return means, st
