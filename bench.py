@@ -12,7 +12,8 @@ its data in the 256 MiB Infinity Cache.  `value` comes from K plain steps; the r
 kernel time from K further steps whose launches each carry dispatch timing events.  Prints
 one JSON line.  --mode selects the other
 workloads of the path (AWQ export, a 128-matrix batch, a percentile-select stress set, the STE
-forward + backward step, and a whole SQWA run), each reported the same way.
+forward + backward step, a whole SQWA run, and the EMA / SWA weight-averaging updates), each
+reported the same way.
 """
 from __future__ import annotations
 
@@ -222,12 +223,50 @@ def workload_sqwa(copies, torch, ops):
                     lambda: [int(sq.status.item()), int(ex.status.item())], cfg, "pgq_table_kernel<1, 5u>"), None
 
 
+def _workload_average(kind, copies, torch, ops):
+    """One EMA update (decay 0.997) or one SWA checkpoint fold (k >= 2) of the 9-layer d=512 fp32
+    weight set per step: read the weights and the fp32 average, write the average."""
+    base = synth.config5_base()
+    numel = sum(t.numel for t in base)
+    rows = sum(t.shape[0] if len(t.shape) == 2 else 1 for t in base)
+    sets = []
+    for k in range(copies):
+        ws = [_dev(t.data, torch) for t in synth.config5_snapshot(k + 1, base)]
+        if kind == "ema":
+            av = ops.Ema(ws, decay=0.997)
+            av.update(ws, init=True)
+        else:
+            av = ops.Swa(ws)
+            av.accumulate(ws, 1)
+        sets.append((av, ws))
+    if kind == "ema":
+        step = lambda i: sets[i % copies][0].update(sets[i % copies][1])  # noqa: E731
+        what = "EMA update (decay 0.997)"
+        kernel = "pgq_table_kernel<4, 1u>"
+    else:
+        step = lambda i: sets[i % copies][0].accumulate(sets[i % copies][1], 2 + i % 15)  # noqa: E731
+        what = "SWA checkpoint fold (running mean, k = 2..16)"
+        kernel = "pgq_table_kernel<5, 1u>"
+    cfg = {"workload": f"{what} of the 9-layer d=512 GPT weight set, fp32 weights and fp32 averages",
+           "tensors": len(base), "params": int(numel)}
+    return Workload(kind, cfg["workload"], 12 * numel, rows, step,
+                    lambda: [int(s[0].status.item()) for s in sets], cfg, kernel), None
+
+
+def workload_ema(copies, torch, ops):
+    return _workload_average("ema", copies, torch, ops)
+
+
+def workload_swa(copies, torch, ops):
+    return _workload_average("swa", copies, torch, ops)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 1000; 50 for --mode sqwa)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 50; 3 for --mode sqwa)")
-    ap.add_argument("--mode", default="export", choices=["export", "awq", "batch", "select", "fakequant", "sqwa"],
+    ap.add_argument("--mode", default="export", choices=["export", "awq", "batch", "select", "fakequant", "sqwa", "ema", "swa"],
                     help="export (default): the 9-layer whole-model export; the others time the remaining "
                          "rows of the path")
     ap.add_argument("--copies", type=int, default=6, help="input/output sets used in rotation")
@@ -250,6 +289,7 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     make = {"export": workload_export, "awq": workload_awq, "batch": workload_batch, "select": workload_select,
+            "ema": workload_ema, "swa": workload_swa,
             "sqwa": workload_sqwa}
     if args.mode == "fakequant":
         wl, tensors = workload_fakequant(args.copies, torch, ops, pgq)

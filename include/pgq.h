@@ -204,6 +204,31 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
                                uint32_t flags, uint32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------------------------ */
+/* Weight averaging without quantization, grouped over n tensors in one launch.               */
+/* w[i]: the weights (fp32 or bf16, rows x cols, row stride ld; awq_s must be NULL; name is    */
+/* ignored).  The averages are caller-owned fp32 device buffers, rows x cols dense, updated in */
+/* place.  workspace: device memory of at least pgq_average_workspace() bytes, 64-byte aligned, */
+/* holding the descriptor table (flags: PGQ_TABLE_RESIDENT as for the other grouped calls).   */
+/* dev_status gets PGQ_DEV_NONFINITE when a weight or an updated average is NaN or infinite.  */
+/* ------------------------------------------------------------------------------------------ */
+pgq_status pgq_average_workspace(const pgq_tensor_in* w, int32_t n, size_t* workspace_bytes);
+
+/* EMA.  Source: "Discriminative TTT + SLOT-24" (PR #1414) and PR #1202 cards, section Weight   */
+/* Averaging: EMA with decay 0.997.  ema = fp32(fp32(decay * ema) + fp32(c * w)) with          */
+/* c = fp32(1 - decay) (binary32, no fused multiply-add); init != 0 sets ema = w instead.     */
+/* decay must lie in [0, 1] (PGQ_ERR_PARAM otherwise).                                        */
+pgq_status pgq_ema_update(const pgq_tensor_in* w, int32_t n, float* const* ema, float decay, int32_t init,
+                          void* workspace, size_t workspace_bytes, uint32_t flags, uint32_t* dev_status,
+                          void* stream);
+
+/* SWA.  Source: "SubSixteen v2" card (PR #69), Novel Contributions and Weight Averaging:      */
+/* stochastic weight averaging over 16 checkpoints.  Fold checkpoint k (1-based, k <= 2^24)    */
+/* into the running mean: mean = w (k = 1), else fp32(mean + fp32(fp32(w - mean) / k)) -- the  */
+/* SQWA update applied to the weights themselves.  Which steps are checkpoints is the caller's. */
+pgq_status pgq_swa_accumulate(const pgq_tensor_in* w, int32_t n, float* const* mean, int32_t k, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, uint32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
 /* Timing aid (no method step): the next kernel launch made by this host thread through any    */
 /* pgq_* call records start_event when that kernel begins executing and stop_event when it     */
 /* completes, from the kernel's own dispatch (hipExtLaunchKernel), so the pair times the kernel */

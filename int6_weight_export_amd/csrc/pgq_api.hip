@@ -136,6 +136,13 @@ uint32_t features_of(const Desc& d)
     return f;
 }
 
+// Weight averaging reads only the input dtype and the vector flag.
+uint32_t features_avg(const Desc& d)
+{
+    if (d.rows <= 0 || d.cols <= 0) return 0;
+    return (d.in_dtype == IN_F32 ? F_F32 : F_BF16) | ((d.flags & DF_VEC) ? 0u : F_SCALAR);
+}
+
 Desc blank_desc()
 {
     Desc d;
@@ -163,10 +170,10 @@ uint32_t grid_for(int mode, uint32_t need, bool table, uint32_t n_tiles)
     {
         std::lock_guard<std::mutex> lk(g_limits.mu);
         if ((int)g_limits.per_cu.size() <= dev) {
-            g_limits.per_cu.resize(dev + 1, std::vector<int>(2 * 4 * 128, -1));
+            g_limits.per_cu.resize(dev + 1, std::vector<int>(2 * kModes * 128, -1));
             g_limits.n_cu.resize(dev + 1, -1);
         }
-        int& slot = g_limits.per_cu[dev][(table ? 512 : 0) + mode * 128 + variant_of(mode, need)];
+        int& slot = g_limits.per_cu[dev][(table ? kModes * 128 : 0) + mode * 128 + variant_of(mode, need)];
         if (slot < 0 || g_limits.n_cu[dev] < 0) {
             int pc = 0, nc = 0;
             if (max_resident_blocks(mode, need, table, &pc, &nc) != 0 || pc <= 0 || nc <= 0) { pc = 4; nc = 256; }
@@ -194,7 +201,7 @@ void set_grouping(Desc& d, int mode)
 {
     int R = 1;
     d.nch = 0;
-    if (mode != MODE_FQ_BWD && d.kind != KIND_F16 && d.cols > 0) {
+    if (mode != MODE_FQ_BWD && mode != MODE_EMA && mode != MODE_SWA && d.kind != KIND_F16 && d.cols > 0) {
         const bool vec = (d.flags & DF_VEC) != 0;
         const int64_t nchunk = vec ? d.cols / (d.in_dtype == IN_F32 ? 4 : 8) : d.cols;
         const int ncht = vec ? (d.in_dtype == IN_F32 ? 8 : 4) : 16;
@@ -243,7 +250,8 @@ pgq_status hip_failed(hipError_t e)
 
 // Build the table on the host, upload it (unless resident) and launch one grouped kernel.
 pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, size_t ws_bytes,
-                       uint32_t flags, uint32_t* dev_status, int sqwa_k, int fq_mode, void* stream)
+                       uint32_t flags, uint32_t* dev_status, int sqwa_k, int fq_mode, void* stream,
+                       int avg_init = 0, float avg_d = 0.0f, float avg_c = 0.0f)
 {
     // Longest tiles first: workgroups start in tile order, so the launch ends on the shortest
     // tiles and its tail is short.  (The tensors' order has no other meaning to the kernel.)
@@ -305,8 +313,12 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
     ka.n_tiles = (uint32_t)total;
     ka.sqwa_k = sqwa_k;
     ka.fq_mode = fq_mode;
+    ka.avg_init = avg_init;
+    ka.avg_d = avg_d;
+    ka.avg_c = avg_c;
+    const bool averaging = mode == MODE_EMA || mode == MODE_SWA;
     uint32_t feats = 0;
-    for (const Desc& d : descs) feats |= features_of(d);
+    for (const Desc& d : descs) feats |= averaging ? features_avg(d) : features_of(d);
     const uint32_t grid = grid_for(mode, feats, true, ka.n_tiles);
     if (const int e = launch(mode, feats, ka, nullptr, grid, stream)) return hip_failed((hipError_t)e);
     if (const hipError_t e = hipGetLastError()) return hip_failed(e);
@@ -348,6 +360,32 @@ pgq_status check_tensor_in(const pgq_tensor_in& t)
     if (t.rows > 0 && t.cols > 0 && !t.w) return PGQ_ERR_NULL;
     if (t.w && !aligned(t.w, esize(t.dtype))) return PGQ_ERR_ALIGN;
     if (t.awq_s && !aligned(t.awq_s, 4)) return PGQ_ERR_ALIGN;
+    return PGQ_OK;
+}
+
+// Descriptors of a weight-averaging call: weights in, fp32 state rows x cols (dense) in place.
+pgq_status average_descs(const pgq_tensor_in* w, int32_t n, float* const* state, int mode,
+                         std::vector<Desc>& descs)
+{
+    descs.assign((size_t)n, blank_desc());
+    for (int32_t i = 0; i < n; ++i) {
+        const pgq_status st = check_tensor_in(w[i]);
+        if (st != PGQ_OK) return st;
+        if (w[i].awq_s) return PGQ_ERR_PARAM;
+        Desc& d = descs[i];
+        d.w = w[i].w;
+        d.in_dtype = w[i].dtype == PGQ_F32 ? IN_F32 : IN_BF16;
+        d.rows = w[i].rows;
+        d.cols = w[i].cols;
+        d.ld = w[i].ld;
+        if (d.rows > 0 && d.cols > 0) {
+            if (!state[i]) return PGQ_ERR_NULL;
+            if (!aligned(state[i], 4)) return PGQ_ERR_ALIGN;
+        }
+        d.mean = state[i];
+        set_vec_flag(d);
+        set_grouping(d, mode);
+    }
     return PGQ_OK;
 }
 
@@ -632,6 +670,49 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
         set_grouping(descs[i], MODE_SQWA);
     }
     return run_grouped(MODE_SQWA, descs, workspace, workspace_bytes, flags, dev_status, k, 0, stream);
+}
+
+pgq_status pgq_average_workspace(const pgq_tensor_in* t, int32_t n, size_t* workspace_bytes)
+{
+    if (!workspace_bytes) return PGQ_ERR_NULL;
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (n > 0 && !t) return PGQ_ERR_NULL;
+    uint64_t nt = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (!shape_ok(t[i].rows, t[i].cols, t[i].ld)) return PGQ_ERR_SHAPE;
+        nt += max_tiles_for(t[i].rows, t[i].cols);
+    }
+    *workspace_bytes = table_bytes((size_t)n, nt);
+    return PGQ_OK;
+}
+
+pgq_status pgq_ema_update(const pgq_tensor_in* w, int32_t n, float* const* ema, float decay, int32_t init,
+                          void* workspace, size_t workspace_bytes, uint32_t flags, uint32_t* dev_status,
+                          void* stream)
+{
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (!(decay >= 0.0f && decay <= 1.0f)) return PGQ_ERR_PARAM;
+    if (n == 0) return PGQ_OK;
+    if (!w || !ema) return PGQ_ERR_NULL;
+    std::vector<Desc> descs;
+    const pgq_status st = average_descs(w, n, ema, MODE_EMA, descs);
+    if (st != PGQ_OK) return st;
+    const float c = 1.0f - decay;              // binary32, formed once
+    return run_grouped(MODE_EMA, descs, workspace, workspace_bytes, flags, dev_status, 0, 0, stream,
+                       init ? 1 : 0, decay, c);
+}
+
+pgq_status pgq_swa_accumulate(const pgq_tensor_in* w, int32_t n, float* const* mean, int32_t k, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, uint32_t* dev_status, void* stream)
+{
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (k < 1 || k > (1 << 24)) return PGQ_ERR_PARAM;     // k must be exact in binary32
+    if (n == 0) return PGQ_OK;
+    if (!w || !mean) return PGQ_ERR_NULL;
+    std::vector<Desc> descs;
+    const pgq_status st = average_descs(w, n, mean, MODE_SWA, descs);
+    if (st != PGQ_OK) return st;
+    return run_grouped(MODE_SWA, descs, workspace, workspace_bytes, flags, dev_status, k, 0, stream);
 }
 
 }  // extern "C"

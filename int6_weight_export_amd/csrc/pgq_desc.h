@@ -14,7 +14,8 @@ constexpr int kWaves = 4;                 // wavefronts per workgroup
 constexpr int kBlock = 64 * kWaves;       // threads per workgroup
 constexpr uint64_t kTableMagic = 0x5047515441424c31ull;   // "PGQTABL1"
 
-enum Mode : int32_t { MODE_EXPORT = 0, MODE_SQWA = 1, MODE_FQ = 2, MODE_FQ_BWD = 3 };
+enum Mode : int32_t { MODE_EXPORT = 0, MODE_SQWA = 1, MODE_FQ = 2, MODE_FQ_BWD = 3, MODE_EMA = 4, MODE_SWA = 5 };
+constexpr int kModes = 6;
 enum : int32_t { IN_F32 = 0, IN_BF16 = 1 };
 enum : int32_t { KIND_F16 = 16 };
 enum : uint32_t { DF_VEC = 1u };          // 16-byte vector path allowed for this tensor
@@ -41,7 +42,7 @@ struct alignas(16) Desc {
     const float* awq_s;       // cols activation scales (AWQ) or null
     uint16_t* awq_out;        // cols fp16 multipliers a_j or null
     uint16_t* f16_out;        // passthrough: rows x cols fp16, dense
-    float* mean;              // SQWA running mean, rows x cols dense
+    float* mean;              // SQWA / SWA running mean or EMA state, rows x cols dense
     const uint16_t* grad;     // STE backward input (bf16, dense)
     uint16_t* grad_out;       // STE backward output (bf16, dense)
     uint8_t* mask;            // STE mask bits, rows x ceil(cols/8)
@@ -73,8 +74,11 @@ struct KArgs {
     uint64_t checksum;
     uint32_t* status;
     uint32_t n_tiles;
-    int32_t sqwa_k;
+    int32_t sqwa_k;               // SQWA / SWA: 1-based snapshot index
     int32_t fq_mode;              // PGQ_FQ_* for MODE_FQ
+    int32_t avg_init;             // EMA: nonzero starts the average at the weights
+    float avg_d;                  // EMA: decay d
+    float avg_c;                  // EMA: fl32(1 - d)
     int32_t reserved;
 };
 

@@ -218,6 +218,21 @@ __device__ __forceinline__ void load_u16(const GLB uint16_t* base, uint32_t e, u
 
 // ---- the clip: the r-th largest magnitude key of the row (keys = |x| bit patterns) -------------
 // `each(f)` calls f(key, valid) for every element slot this lane owns.
+// The k-th largest (1 <= k <= 64) of the 64 values the lanes hold: a lane whose value has fewer
+// than k values above it and at least k at or above it holds the answer.  All lanes active.
+__device__ __forceinline__ uint32_t rank_select64(uint32_t v, uint32_t k)
+{
+    uint32_t gt = 0, ge = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+        const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+        gt += u > v ? 1u : 0u;
+        ge += u >= v ? 1u : 0u;
+    }
+    const uint64_t hit = __ballot(gt < k && k <= ge);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)__builtin_ctzll(hit));
+}
+
 template <class Each>
 __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t* hist, int lane)
 {
@@ -241,6 +256,33 @@ __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t
             m = wave_max(below);
         }
         return m;
+    }
+    if (r <= 64) {
+        // candidate select.  The r-th largest of the 64 lane maxima, t0, is a lower bound of the
+        // answer (those r maxima are elements >= t0), so the answer is the r-th largest of the
+        // elements >= t0.  When there are at most 64 of them (the usual case for r <= 64 unless
+        // many keys tie), they are packed one per lane through LDS and ranked directly.
+        uint32_t lm = 0;                       // a lane with no element offers 0 (<= every key)
+        each([&](uint32_t k, bool ok) { if (ok) lm = max(lm, k); });
+        const uint32_t t0 = rank_select64(lm, (uint32_t)r);
+        uint32_t c = 0;
+        each([&](uint32_t k, bool ok) { c += (ok && k >= t0) ? 1u : 0u; });
+        c = wave_sum(c);
+        if (c <= 64) {
+            uint32_t base = 0;                 // uniform: candidates already packed
+            each([&](uint32_t k, bool ok) {
+                const bool cand = ok && k >= t0;
+                const uint64_t b = __ballot(cand);
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+                if (cand) hist[base + below] = k;
+                base += (uint32_t)__builtin_popcountll(b);
+            });
+            lds_sync_wave();
+            const uint32_t v = (uint32_t)lane < c ? hist[lane] : 0u;   // padding ranks last
+            lds_sync_wave();
+            return rank_select64(v, (uint32_t)r);
+        }
     }
     // radix select, most significant digit first: bits 30..23, 22..15, 14..7, 6..0, with a
     // 256-bin histogram per wave in LDS
@@ -702,15 +744,19 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         uint32_t ck = mx;
         if constexpr (SEL) {
             if (d.rank_top > 1) {
+                // f runs in uniform control flow (lanes past the row pass ok = false)
                 auto each = [&](auto&& f) {
                     for (int base = 0; base < nchunk; base += 64) {
-                        const uint32_t c = (uint32_t)(base + lane);
-                        if ((int)c < nchunk) {
-                            float x[VEC], a[VEC], ainv[VEC];
+                        const bool ok = base + lane < nchunk;
+                        float x[VEC], a[VEC], ainv[VEC];
+                        if (ok) {
                             load_chunk((uint32_t)base, x, a, ainv, nullptr);
+                        } else {
 #pragma unroll
-                            for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, true);
+                            for (int v = 0; v < VEC; ++v) x[v] = 0.0f;
                         }
+#pragma unroll
+                        for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, ok);
                     }
                 };
                 ck = kth_largest(each, d.rank_top, hist, lane);
@@ -881,6 +927,59 @@ __device__ __forceinline__ void row_fq_bwd(const Desc& d, int64_t row, int lane)
     }
 }
 
+// ---- weight averaging rows: fp32 state rows x cols, dense --------------------------------------
+// EMA (Weight Averaging sections of the PR #1414 / PR #1202 cards, decay 0.997):
+// e = fl32(fl32(d * e) + fl32(c * w)) with c = fl32(1 - d), or e = w on the first update.
+// SWA (PR #69 card, 16 checkpoints): the running mean of the checkpoints, mean = w for k = 1,
+// else fl32(mean + fl32(fl32(w - mean) / k)).  Pure streaming: U chunks per lane in flight.
+template <int MODE, int IN, int VEC>
+__device__ __forceinline__ void row_average(const Desc& d, int64_t row, int lane, const KArgs& ka, uint32_t& st)
+{
+    constexpr int U = VEC >= 8 ? 1 : VEC == 4 ? 2 : 8;
+    const int nchunk = (int)(d.cols / VEC);
+    const size_t esz = IN == IN_F32 ? 4 : 2;
+    const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
+    GLB float* mrow = gp(d.mean) + row * d.cols;
+    const bool copy = MODE == MODE_EMA ? ka.avg_init != 0 : ka.sqwa_k == 1;
+    const float kf = (float)ka.sqwa_k;
+    const uint32_t e = (uint32_t)lane * VEC;
+    for (int base = 0; base < nchunk; base += 64 * U) {
+        float x[U][VEC], m[U][VEC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cb = base + 64 * u;                 // uniform chunk base
+            if (cb + lane < nchunk) {
+                load_x<IN, VEC>(offset_row<IN>(wrow, (uint32_t)(cb * VEC)), e, x[u]);
+                if (!copy) load_f32<VEC>(mrow + cb * VEC, e, m[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cb = base + 64 * u;
+            if (cb + lane < nchunk) {
+                float r[VEC];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    if (copy) {
+                        r[v] = x[u][v];
+                    } else if constexpr (MODE == MODE_EMA) {
+                        const float kept = ka.avg_d * m[u][v];
+                        const float added = ka.avg_c * x[u][v];
+                        r[v] = kept + added;
+                    } else {
+                        const float diff = x[u][v] - m[u][v];
+                        const float step = diff / kf;
+                        r[v] = m[u][v] + step;
+                    }
+                    if (!(fabsf(x[u][v]) <= 3.402823466e38f) || !(fabsf(r[v]) <= 3.402823466e38f))
+                        st |= PGQ_DEV_NONFINITE;
+                }
+                store_f32<VEC>(mrow + cb * VEC, e, r);
+            }
+        }
+    }
+}
+
 template <int MODE, uint32_t F>
 __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nrows, int lane, uint32_t* hist,
                                               const float* awq_lds, const KArgs& ka, uint32_t& st)
@@ -890,7 +989,25 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nr
     constexpr bool LONG = (F & F_LONG) != 0;
     constexpr bool SCALAR = (F & F_SCALAR) != 0;
     const bool vec = (d.flags & DF_VEC) != 0;
-    if constexpr (MODE == MODE_FQ_BWD) {
+    if constexpr (MODE == MODE_EMA || MODE == MODE_SWA) {
+        for (int r = 0; r < nrows; ++r) {
+            if constexpr ((F & F_F32) != 0) {
+                if (d.in_dtype == IN_F32) {
+                    if constexpr (SCALAR) {
+                        if (!vec) { row_average<MODE, IN_F32, 1>(d, row + r, lane, ka, st); continue; }
+                    }
+                    row_average<MODE, IN_F32, 4>(d, row + r, lane, ka, st);
+                    continue;
+                }
+            }
+            if constexpr ((F & F_BF16) != 0) {
+                if constexpr (SCALAR) {
+                    if (!vec) { row_average<MODE, IN_BF16, 1>(d, row + r, lane, ka, st); continue; }
+                }
+                row_average<MODE, IN_BF16, 8>(d, row + r, lane, ka, st);
+            }
+        }
+    } else if constexpr (MODE == MODE_FQ_BWD) {
         for (int r = 0; r < nrows; ++r) {
             if (vec) row_fq_bwd<8>(d, row + r, lane);
             else row_fq_bwd<1>(d, row + r, lane);
@@ -988,7 +1105,7 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
     asm volatile("" ::"s"(d.rows), "s"(d.cols), "s"(d.ld), "s"(d.kind), "s"(d.flags), "s"(d.rgroup),
                  "s"(d.tile_rows), "s"(d.nch), "s"(d.w), "s"(d.Q));
     if constexpr (MODE == MODE_EXPORT) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.dq_dtype));
-    if constexpr (MODE == MODE_SQWA) asm volatile("" ::"s"(d.mean));
+    if constexpr (MODE == MODE_SQWA || MODE == MODE_EMA || MODE == MODE_SWA) asm volatile("" ::"s"(d.mean));
     if constexpr (MODE == MODE_FQ || MODE == MODE_FQ_BWD)
         asm volatile("" ::"s"(d.dq), "s"(d.scales), "s"(d.mask), "s"(d.grad), "s"(d.grad_out));
     if constexpr ((F & F_PASS) != 0 && MODE == MODE_EXPORT) asm volatile("" ::"s"(d.f16_out));
@@ -1071,6 +1188,20 @@ const void* kernel_ptr(bool table)
 constexpr uint32_t kExportVariants[] = {F_F32 | F_PASS, F_BF16 | F_PASS, F_F32 | F_PASS | F_AWQ,
                                         F_F32 | F_PASS | F_SEL, F_ALL};
 constexpr uint32_t kFqVariants[] = {F_BF16, F_BF16 | F_SEL, F_ALL};
+constexpr uint32_t kAvgAll = F_F32 | F_BF16 | F_SCALAR;
+constexpr uint32_t kAvgVariants[] = {F_F32, F_BF16, kAvgAll};
+
+// Weight averaging runs as grouped launches only.
+template <int MODE>
+const void* average_kernel(uint32_t v, bool table)
+{
+    if (!table) return nullptr;
+    switch (v) {
+    case F_F32: return reinterpret_cast<const void*>(&pgq_table_kernel<MODE, F_F32>);
+    case F_BF16: return reinterpret_cast<const void*>(&pgq_table_kernel<MODE, F_BF16>);
+    default: return reinterpret_cast<const void*>(&pgq_table_kernel<MODE, kAvgAll>);
+    }
+}
 
 template <int MODE>
 const void* export_like(uint32_t v, bool table)
@@ -1095,6 +1226,8 @@ const void* pick(int mode, uint32_t need, bool table)
         if (v == (F_BF16 | F_SEL)) return kernel_ptr<MODE_FQ, F_BF16 | F_SEL>(table);
         return kernel_ptr<MODE_FQ, F_ALL>(table);
     case MODE_FQ_BWD: return kernel_ptr<MODE_FQ_BWD, F_ALL>(table);
+    case MODE_EMA: return average_kernel<MODE_EMA>(v, table);
+    case MODE_SWA: return average_kernel<MODE_SWA>(v, table);
     default: return nullptr;
     }
 }
@@ -1109,6 +1242,10 @@ uint32_t variant_of(int mode, uint32_t need)
     } else if (mode == MODE_FQ) {
         for (uint32_t v : kFqVariants)
             if ((need & ~v) == 0) return v;
+    } else if (mode == MODE_EMA || mode == MODE_SWA) {
+        for (uint32_t v : kAvgVariants)
+            if ((need & ~v) == 0) return v;
+        return kAvgAll;
     }
     return F_ALL;
 }

@@ -263,3 +263,56 @@ class Sqwa:
     def exporter(self, want_dq: bool = False) -> Exporter:
         return Exporter([ExportTensor(t.name, m, t.awq_s) for t, m in zip(self.exporter_template, self.means)],
                         self.policy, want_dq=want_dq)
+
+
+class _Averager:
+    """fp32 averages of a fixed list of weight tensors (fp32 or bf16, rows contiguous), updated
+    in place by one grouped launch per call.  The tensor array and the workspace holding the
+    uploaded descriptor table are kept per weight buffer set, so calls over resident weights
+    only re-enqueue the kernel."""
+
+    def __init__(self, like: Sequence[torch.Tensor]):
+        like = list(like)
+        self.n = len(like)
+        dev = like[0].device
+        self.avg = [torch.empty(w.shape, dtype=torch.float32, device=dev) for w in like]
+        self.avg_ptrs = (ctypes.c_void_p * self.n)(*[a.data_ptr() for a in self.avg])
+        self.status = new_status(dev)
+        self._tables: Dict[tuple, tuple] = {}
+
+    def _table(self, weights: Sequence[torch.Tensor], reuse_table: bool):
+        key = tuple(w.data_ptr() for w in weights)
+        cached = self._tables.get(key)
+        if cached is not None and reuse_table:
+            return cached + (pgq.PGQ_TABLE_RESIDENT,)
+        assert len(weights) == self.n
+        arr, keep = _tensor_in_array([ExportTensor("", w) for w in weights])
+        wb = ctypes.c_size_t(0)
+        pgq.check(pgq.pgq_average_workspace(arr, self.n, ctypes.byref(wb)), "pgq_average_workspace")
+        ws = torch.empty(max(wb.value, 64), dtype=torch.uint8, device=self.avg[0].device)
+        self._tables[key] = (arr, keep, ws)
+        return arr, keep, ws, 0
+
+
+class Ema(_Averager):
+    """Exponential moving average of the weights (decay 0.997 by default)."""
+
+    def __init__(self, like: Sequence[torch.Tensor], decay: float = 0.997):
+        super().__init__(like)
+        self.decay = decay
+
+    def update(self, weights: Sequence[torch.Tensor], init: bool = False, reuse_table: bool = True):
+        arr, _, ws, flags = self._table(weights, reuse_table)
+        rc = pgq.pgq_ema_update(arr, self.n, self.avg_ptrs, self.decay, 1 if init else 0, _p(ws), ws.numel(),
+                                flags, _p(self.status), _stream())
+        pgq.check(rc, "pgq_ema_update")
+
+
+class Swa(_Averager):
+    """Running mean of weight checkpoints k = 1, 2, ... (stochastic weight averaging)."""
+
+    def accumulate(self, weights: Sequence[torch.Tensor], k: int, reuse_table: bool = True):
+        arr, _, ws, flags = self._table(weights, reuse_table)
+        rc = pgq.pgq_swa_accumulate(arr, self.n, self.avg_ptrs, k, _p(ws), ws.numel(), flags, _p(self.status),
+                                    _stream())
+        pgq.check(rc, "pgq_swa_accumulate")

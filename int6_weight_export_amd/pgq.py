@@ -91,6 +91,11 @@ SIGNATURES = {
                                 ctypes.POINTER(_P), _P, _SZ, _U32, _P, _P]),
     "pgq_sqwa_accumulate": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan),
                                    ctypes.POINTER(_P), _I32, _P, _SZ, _U32, _P, _P]),
+    "pgq_average_workspace": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(_SZ)]),
+    "pgq_ema_update": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(_P), ctypes.c_float, _I32, _P,
+                              _SZ, _U32, _P, _P]),
+    "pgq_swa_accumulate": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(_P), _I32, _P, _SZ, _U32,
+                                  _P, _P]),
     "pgq_time_next_launch": (_I32, [_P, _P]),
     "pgq_status_str": (ctypes.c_char_p, [_I32]),
     "pgq_version": (ctypes.c_char_p, []),
@@ -147,6 +152,18 @@ def pgq_export_model(t, n, plan, arena, dq_out, workspace, workspace_bytes, flag
 def pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status, stream):
     return _lib.pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status,
                                     stream)
+
+
+def pgq_average_workspace(w, n, workspace_bytes):
+    return _lib.pgq_average_workspace(w, n, workspace_bytes)
+
+
+def pgq_ema_update(w, n, ema, decay, init, workspace, workspace_bytes, flags, dev_status, stream):
+    return _lib.pgq_ema_update(w, n, ema, decay, init, workspace, workspace_bytes, flags, dev_status, stream)
+
+
+def pgq_swa_accumulate(w, n, mean, k, workspace, workspace_bytes, flags, dev_status, stream):
+    return _lib.pgq_swa_accumulate(w, n, mean, k, workspace, workspace_bytes, flags, dev_status, stream)
 
 
 def pgq_time_next_launch(start_event, stop_event):

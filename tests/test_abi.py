@@ -173,3 +173,34 @@ def test_export_and_sqwa_argument_errors():
     arr[1].dtype = 4
     assert pgq.pgq_export_plan(arr, 3, ctypes.byref(pol), plan, ctypes.byref(ab),
                                ctypes.byref(wb)) == pgq.PGQ_ERR_DTYPE
+
+
+def test_average_argument_errors():
+    ts = synth.config2()[:4]
+    arr, keep = _tensor_array(ts)
+    wb = ctypes.c_size_t(0)
+    assert pgq.pgq_average_workspace(arr, 4, ctypes.byref(wb)) == 0 and wb.value > 64
+    assert pgq.pgq_average_workspace(arr, 4, None) == pgq.PGQ_ERR_NULL
+    assert pgq.pgq_average_workspace(arr, -1, ctypes.byref(wb)) == pgq.PGQ_ERR_SHAPE
+    st = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    ema, swa = pgq.pgq_ema_update, pgq.pgq_swa_accumulate
+    assert ema(arr, 0, st, 0.997, 0, None, 0, 0, None, None) == pgq.PGQ_OK        # nothing to do
+    for bad in (-0.5, 1.5, float("nan")):
+        assert ema(arr, 4, st, bad, 0, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM
+    assert ema(arr, 4, None, 0.997, 0, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_NULL
+    assert ema(arr, -2, st, 0.997, 0, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_SHAPE
+    assert ema(arr, 4, st, 0.997, 0, FAKE, 64, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
+    assert ema(arr, 4, st, 0.997, 0, FAKE + 4, wb.value, 0, None, None) == pgq.PGQ_ERR_ALIGN
+    for k in (0, -1, (1 << 24) + 1):
+        assert swa(arr, 4, st, k, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM
+    assert swa(arr, 4, st, 2, FAKE, 64, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
+    st[2] = FAKE + 2                                                                # misaligned average
+    assert swa(arr, 4, st, 2, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_ALIGN
+    st[2] = None
+    assert swa(arr, 4, st, 2, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_NULL
+    st[2] = FAKE
+    arr[1].awq_s = FAKE                                                             # no AWQ here
+    assert ema(arr, 4, st, 0.997, 0, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM
+    arr[1].awq_s = 0
+    arr[3].dtype = 9
+    assert swa(arr, 4, st, 2, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_DTYPE

@@ -301,6 +301,27 @@ def test_sqwa_resume_equals_uninterrupted():
 
 
 # ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cols", [700, 1536, 3000])
+def test_select_every_rank_path(cols):
+    """Exact order statistics for ranks on both sides of each select strategy (iterated maximum
+    up to 8, candidate packing up to 64, radix above), on continuous rows, rows with heavy ties
+    (a 7-value alphabet, so more than 64 keys can tie at the bound) and sparse spiky rows."""
+    rng = np.random.default_rng(cols)
+    cont = (rng.standard_normal((4, cols)) * 0.02).astype(np.float32)
+    ties = (rng.integers(-3, 4, (4, cols)) * 0.01).astype(np.float32)
+    spiky = np.zeros((4, cols), np.float32)
+    for r in range(4):
+        idx = rng.choice(cols, 40 + 10 * r, replace=False)
+        spiky[r, idx] = (rng.standard_normal(idx.size) * (r + 1)).astype(np.float32)
+    w = np.concatenate([cont, ties, spiky])
+    for rank in [1, 2, 7, 8, 9, 16, 33, 40, 63, 64, 65, 100]:
+        say(f"select {w.shape[0]}x{cols} rank {rank}")
+        num, den = cols - rank + 1, cols             # k = n - rank + 1: the rank-th largest |w|
+        out = ops.quantize_rows(dev(w), bits=6, pct=(num, den))
+        torch.cuda.synchronize()
+        _check_rows(w, out, 31, num, den, f"select {cols} rank {rank}")
+
+
 def test_edge_rows_and_status_bits():
     say("edge rows: zeros, spike, constant, grid, ties, tiny")
     n = 512
