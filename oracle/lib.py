@@ -57,6 +57,8 @@ def load():
             lib.orc_percentile_rank.restype = _I64
             lib.orc_quantize_rows.argtypes = [_P, _I64, _I64, _I64, _I32, _U32, _U32, _P, _P, _P, _P, _P, _P]
             lib.orc_quantize_rows.restype = _U32
+            lib.orc_quantize_tensor.argtypes = [_P, _I64, _I64, _I64, _I32, _U32, _U32, _P, _P, _P, _P]
+            lib.orc_quantize_tensor.restype = _U32
             lib.orc_awq_multipliers.argtypes = [_P, _I64, _P]
             lib.orc_awq_multipliers.restype = _U32
             lib.orc_fakequant_rows.argtypes = [_P, _I64, _I64, _I64, _I32, _U32, _U32, _P, _P, _P, _P, _P, _P]
@@ -137,6 +139,23 @@ def quantize_rows(w, Q: int, num: int = 1, den: int = 1, awq=None, want_t: bool 
     if want_clip:
         out["clip"] = clip
     return out
+
+
+def quantize_tensor(w, Q: int, num: int = 1, den: int = 1) -> dict:
+    """Per-tensor quantization of a 2-D float32 array: one fp16 scale for all rows * cols.
+
+    Returns dict(codes int8 [rows, cols], scale uint16 [1], dq float32 [rows, cols], clip
+    float32, status)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    assert w.ndim == 2 and w.size > 0
+    rows, cols = w.shape
+    codes = np.empty((rows, cols), dtype=np.int8)
+    scale = np.empty(1, dtype=np.uint16)
+    dq = np.empty((rows, cols), dtype=np.float32)
+    clip = np.empty(1, dtype=np.float32)
+    st = load().orc_quantize_tensor(_ptr(w), rows, cols, cols, Q, num, den, _ptr(codes), _ptr(scale), _ptr(dq),
+                                    _ptr(clip))
+    return dict(codes=codes, scale=scale, dq=dq, clip=float(clip[0]), status=int(st))
 
 
 def awq_multipliers(s):

@@ -212,6 +212,23 @@ uint32_t orc_quantize_rows(const float* w, int64_t rows, int64_t cols, int64_t l
     return st;
 }
 
+/* Per-tensor quantization ("Per-row / per-tensor quantization strategy" with "Percentile
+ * clipping for stable int8 export", PR #2159 Key Explored Modifications): one scale for the
+ * whole tensor, the clip being the k-th smallest |w| over all rows * cols elements.  That is
+ * the row quantizer applied to the tensor read as one row; codes / dq are dense rows x cols. */
+uint32_t orc_quantize_tensor(const float* w, int64_t rows, int64_t cols, int64_t ld, int32_t Q,
+                             uint32_t num, uint32_t den, int8_t* codes, uint16_t* scale, float* dq,
+                             float* clip)
+{
+    int64_t n = rows * cols;
+    float* flat = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j) flat[r * cols + j] = w[r * ld + j];
+    uint32_t st = orc_quantize_row(flat, n, Q, num, den, NULL, codes, scale, dq, NULL, clip);
+    free(flat);
+    return st;
+}
+
 /* AWQ column multipliers a_j = fp16_rne(sqrt(s_j)) (exponent 1/2), s_j > 0 and finite. */
 uint32_t orc_awq_multipliers(const float* s, int64_t cols, uint16_t* a)
 {

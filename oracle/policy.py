@@ -41,6 +41,7 @@ class Policy:
     passthrough_below: int = 65536
     q6: Tuple[int, int, int] = (6, 9999, 10000)   # (bits, pct_num, pct_den)
     q8: Tuple[int, int, int] = (8, 1, 1)
+    per_tensor: bool = False                      # one scale per integer-kind tensor
 
 
 def qmax(bits: int) -> int:
@@ -92,7 +93,13 @@ def export(tensors, pol: Policy, awq: Optional[Dict[str, np.ndarray]] = None) ->
             if s is not None and kind == KIND_INT6:
                 a, st = lib.awq_multipliers(s)
                 rec["awq"] = a
-            r = lib.quantize_rows(w.reshape(rows, cols), Q, num, den, awq=a)
+            if pol.per_tensor:
+                if a is not None:
+                    raise ValueError("AWQ and per-tensor scales do not combine")
+                r = lib.quantize_tensor(w.reshape(rows, cols), Q, num, den)
+                r["scales"] = r["scale"]
+            else:
+                r = lib.quantize_rows(w.reshape(rows, cols), Q, num, den, awq=a)
             rec.update(codes=r["codes"], scales=r["scales"], dq=r["dq"].reshape(w.shape),
                        status=st | r["status"])
         out.append(rec)
