@@ -47,11 +47,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def algorithmic_bytes(tensors, want_dq: bool) -> dict:
+def algorithmic_bytes(tensors, want_dq: bool, per_tensor: bool = False) -> dict:
     """Bytes each launch must move at least once: inputs read, outputs written."""
     import oracle
 
-    pol = oracle.Policy()
+    pol = oracle.Policy(per_tensor=per_tensor)
     b_in = b_codes = b_scales = b_f16 = b_dq = 0
     rows_total = 0
     for t in tensors:
@@ -62,7 +62,7 @@ def algorithmic_bytes(tensors, want_dq: bool) -> dict:
             b_f16 += 2 * t.numel
         else:
             b_codes += t.numel
-            b_scales += 2 * rows
+            b_scales += 2 * (1 if per_tensor else rows)
             rows_total += rows
         if want_dq:
             b_dq += 4 * t.numel
@@ -223,6 +223,27 @@ def workload_sqwa(copies, torch, ops):
                     lambda: [int(sq.status.item()), int(ex.status.item())], cfg, "pgq_table_kernel<1, 5u>"), None
 
 
+def workload_tensor(copies, torch, ops):
+    """Per-tensor scales: the 9-layer export with one scale per integer tensor, the clip at the
+    99.99th percentile of |w| over the whole tensor (int8 tok_emb: absmax).  A step is the
+    call's five launches (four radix select passes, then the quantize pass)."""
+    tensors = synth.config2()
+    ab = algorithmic_bytes(tensors, want_dq=True, per_tensor=True)
+    sets = []
+    for _ in range(copies):
+        ex = ops.Exporter([ops.ExportTensor(t.name, _dev(t.data, torch)) for t in tensors],
+                          ops.make_policy(per_tensor=True), want_dq=True)
+        ex.run()
+        sets.append(ex)
+    cfg = {"workload": "per-tensor export of the 9-layer d=512 GPT weight set: one fp16 scale per tensor, "
+                       "int6 with the clip at the 99.99th percentile of |w| over the tensor (exact multi-"
+                       "workgroup radix select), int8 absmax tok_emb.weight, fp16 vectors, fp32 dequant",
+           "tensors": len(tensors), "params": int(sum(t.numel for t in tensors))}
+    return Workload("tensor", cfg["workload"], ab["total"], ab["rows"], lambda i: sets[i % len(sets)].run(),
+                    lambda: [int(s.status.item()) for s in sets], cfg,
+                    "pgq_table_kernel<6, 1u> x4 + pgq_table_kernel<0, 5u>"), tensors
+
+
 def _workload_average(kind, copies, torch, ops):
     """One EMA update (decay 0.997) or one SWA checkpoint fold (k >= 2) of the 9-layer d=512 fp32
     weight set per step: read the weights and the fp32 average, write the average."""
@@ -266,7 +287,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 1000; 50 for --mode sqwa)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 50; 3 for --mode sqwa)")
-    ap.add_argument("--mode", default="export", choices=["export", "awq", "batch", "select", "fakequant", "sqwa", "ema", "swa"],
+    ap.add_argument("--mode", default="export", choices=["export", "awq", "batch", "select", "fakequant", "sqwa", "ema", "swa", "tensor"],
                     help="export (default): the 9-layer whole-model export; the others time the remaining "
                          "rows of the path")
     ap.add_argument("--copies", type=int, default=6, help="input/output sets used in rotation")
@@ -289,7 +310,7 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     make = {"export": workload_export, "awq": workload_awq, "batch": workload_batch, "select": workload_select,
-            "ema": workload_ema, "swa": workload_swa,
+            "ema": workload_ema, "swa": workload_swa, "tensor": workload_tensor,
             "sqwa": workload_sqwa}
     if args.mode == "fakequant":
         wl, tensors = workload_fakequant(args.copies, torch, ops, pgq)

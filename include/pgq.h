@@ -162,7 +162,10 @@ typedef struct {
     const char* const* int8_patterns; /* host array of n_patterns host strings; a tensor whose name
                                          contains one of them (substring) uses q_sensitive */
     int32_t n_patterns;
-    int32_t reserved;
+    int32_t per_tensor;               /* 0: one scale per row; 1: one scale per integer-kind tensor,
+                                         its clip the percentile of |w| over the whole tensor
+                                         (PR #2159 Key Explored Modifications: per-row / per-tensor
+                                         quantization, percentile clipping).  Not with AWQ. */
     int64_t passthrough_below;        /* tensors with fewer elements are stored as fp16 (65536) */
     pgq_qparams q_default;            /* e.g. {6, 9999, 10000} */
     pgq_qparams q_sensitive;          /* e.g. {8, 1, 1} */
@@ -172,6 +175,7 @@ typedef struct {
     int32_t kind;           /* PGQ_KIND_F16, or the code width in bits */
     int32_t has_awq;        /* 1 when AWQ multipliers are produced for this tensor */
     pgq_qparams qp;         /* quantizer of an integer kind */
+    int32_t per_tensor;     /* 1: one scale for the whole tensor (scales region holds 1 fp16) */
     int64_t codes_off;      /* byte offsets into the arena; -1 when absent */
     int64_t scales_off;
     int64_t f16_off;
@@ -181,13 +185,18 @@ typedef struct {
 /* Host only (no device work): decide each tensor's kind and lay out the output arena.
  * plan: host array of n entries (written).  arena_bytes / workspace_bytes: sizes the
  * caller must allocate for pgq_export_model / pgq_sqwa_accumulate.  Regions are 256-byte
- * aligned: codes rows x cols int8, scales rows fp16, f16 numel fp16, awq cols fp16. */
+ * aligned: codes rows x cols int8, scales rows fp16 (1 when per_tensor), f16 numel fp16, awq
+ * cols fp16.  PGQ_ERR_PARAM when per_tensor meets AWQ scales; PGQ_ERR_SHAPE when a per-tensor
+ * tensor has 2^32 elements or more. */
 pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* pol,
                            pgq_tensor_plan* plan, size_t* arena_bytes, size_t* workspace_bytes);
 
 /* Quantize every tensor into the arena in one launch.  dq_out: NULL, or a host array of n
  * device pointers (each NULL or rows x cols fp32) receiving the value each tensor decodes to
- * (code * s, AWQ-divided, or fp32(fp16) for passthrough). */
+ * (code * s, AWQ-divided, or fp32(fp16) for passthrough).  With per-tensor entries the launch
+ * is preceded by the whole-tensor clip select: one pass for an absmax clip, else four radix
+ * passes, each one launch over those tensors (their select state lives in the workspace).
+ * After an error return, call again without PGQ_TABLE_RESIDENT. */
 pgq_status pgq_export_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan* plan,
                             void* arena, float* const* dq_out, void* workspace, size_t workspace_bytes,
                             uint32_t flags, uint32_t* dev_status, void* stream);
@@ -229,11 +238,11 @@ pgq_status pgq_swa_accumulate(const pgq_tensor_in* w, int32_t n, float* const* m
                               size_t workspace_bytes, uint32_t flags, uint32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------------------------ */
-/* Timing aid (no method step): the next kernel launch made by this host thread through any    */
-/* pgq_* call records start_event when that kernel begins executing and stop_event when it     */
-/* completes, from the kernel's own dispatch (hipExtLaunchKernel), so the pair times the kernel */
-/* alone.  The events are hipEvent_t handles passed as void* (created by the caller, not       */
-/* owned); NULL, NULL clears a pending request.  Applies to exactly one launch.                */
+/* Timing aid (no method step): the next pgq_* call made by this host thread that launches     */
+/* kernels records start_event when its first kernel begins executing and stop_event when its */
+/* last kernel completes, from the kernels' own dispatches (hipExtLaunchKernel), so the pair   */
+/* times the call's kernels alone.  The events are hipEvent_t handles passed as void* (created */
+/* by the caller, not owned); NULL, NULL clears a pending request.  Applies to one call.       */
 /* ------------------------------------------------------------------------------------------ */
 pgq_status pgq_time_next_launch(void* start_event, void* stop_event);
 

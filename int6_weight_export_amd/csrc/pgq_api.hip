@@ -45,6 +45,13 @@ int awq_groups_per_wave()
     return v;
 }
 
+// Export tiles per workgroup of a whole-tensor select pass.
+int sel_group()
+{
+    static const int v = env_int("PGQ_SEL_GROUP", 2, 1, 64);   // measured best of 1, 2, 4, 8
+    return v;
+}
+
 // Upper bound on the rows a wavefront processes together.
 int max_rgroup()
 {
@@ -118,7 +125,7 @@ void set_vec_flag(Desc& d)
     ok = ok && (!d.grad || aligned(d.grad, 16));
     ok = ok && (!d.grad_out || aligned(d.grad_out, 16));
     (void)ein;
-    d.flags = ok ? DF_VEC : 0u;
+    d.flags = (d.flags & ~(uint32_t)DF_VEC) | (ok ? (uint32_t)DF_VEC : 0u);
 }
 
 // Kernel features a tensor needs (see F_* in pgq_desc.h).
@@ -130,7 +137,7 @@ uint32_t features_of(const Desc& d)
     if (!vec) f |= F_SCALAR;
     if (d.kind == KIND_F16) return f | F_PASS;
     if (d.awq_s) f |= F_AWQ;
-    if (d.rank_top > 1) f |= F_SEL;
+    if (d.rank_top > 1 && !(d.flags & DF_TENSOR)) f |= F_SEL;
     const int64_t reg_cols = !vec ? kRegCols_Scalar : (d.in_dtype == IN_F32 ? kRegCols_F32 : kRegCols_BF16);
     if (d.cols > reg_cols) f |= F_LONG;
     return f;
@@ -188,12 +195,28 @@ uint32_t grid_for(int mode, uint32_t need, bool table, uint32_t n_tiles)
     return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(g, n_tiles));
 }
 
-size_t table_bytes(size_t n_desc, uint64_t n_tiles)
+// Workspace layout of a grouped call: header | descriptors | first tile per tensor | tensor per
+// tile | (per-tensor scales) first tile per tensor and tensor per tile of the select passes |
+// one TState per tensor.  The last three parts are uploaded only when a call needs them.
+struct TableLayout {
+    size_t desc_off, start_off, tdesc_off, start2_off, tdesc2_off, state_off, end_main, end;
+};
+
+TableLayout table_layout(size_t n_desc, uint64_t n_tiles)
 {
-    return sizeof(TableHeader) + align_up((int64_t)(n_desc * sizeof(Desc)), 64) +
-           (size_t)align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 64) +
-           (size_t)align_up((int64_t)(n_tiles * sizeof(uint32_t)), 8);
+    TableLayout L;
+    L.desc_off = sizeof(TableHeader);
+    L.start_off = L.desc_off + align_up((int64_t)(n_desc * sizeof(Desc)), 64);
+    L.tdesc_off = L.start_off + align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 64);
+    L.end_main = L.tdesc_off + align_up((int64_t)(n_tiles * sizeof(uint32_t)), 8);
+    L.start2_off = align_up((int64_t)L.end_main, 64);
+    L.tdesc2_off = L.start2_off + align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 64);
+    L.state_off = L.tdesc2_off + align_up((int64_t)(n_tiles * sizeof(uint32_t)), 64);
+    L.end = L.state_off + n_desc * sizeof(TState);
+    return L;
 }
+
+size_t table_bytes(size_t n_desc, uint64_t n_tiles) { return table_layout(n_desc, n_tiles).end; }
 
 // Rows a wavefront loads together: as many as the register tile holds (a power of two), and
 // the exact chunk count per lane of a row on the vector path.
@@ -269,31 +292,51 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
     }
     start[n] = (uint32_t)total;
     if (total == 0) return PGQ_OK;
-    const size_t need = table_bytes(n, total);
+    const TableLayout L = table_layout(n, total);
+    // per-tensor scales: the select passes run over the tiles of those tensors only, sel_group()
+    // export tiles per select workgroup
+    const uint64_t kSelGroup = (uint64_t)sel_group();
+    std::vector<uint32_t> start2(n + 1, 0);
+    uint64_t total2 = 0;
+    int passes = 0;
+    for (size_t i = 0; i < n; ++i) {
+        start2[i] = (uint32_t)total2;
+        if (descs[i].flags & DF_TENSOR) {
+            total2 += (tiles_for(descs[i]) + kSelGroup - 1) / kSelGroup;
+            passes = std::max(passes, descs[i].rank_top > 1 ? 4 : 1);
+            descs[i].tstate = reinterpret_cast<TState*>(static_cast<uint8_t*>(ws) + L.state_off) + i;
+        }
+    }
+    start2[n] = (uint32_t)total2;
+    const size_t need = passes ? L.end : L.end_main;
     if (!ws) return PGQ_ERR_WORKSPACE;
     if (ws_bytes < need) return PGQ_ERR_WORKSPACE;
     if (!aligned(ws, 64)) return PGQ_ERR_ALIGN;
 
-    // The checksum covers the descriptors and the tile prefix (the per-tile descriptor index is
-    // a function of the prefix), so a call on a resident table hashes ~n * 160 bytes and
-    // builds nothing else.
-    const size_t desc_off = sizeof(TableHeader);
-    const size_t start_off = desc_off + align_up((int64_t)(n * sizeof(Desc)), 64);
-    const size_t tdesc_off = start_off + align_up((int64_t)((n + 1) * sizeof(uint32_t)), 64);
+    // The checksum covers the descriptors and both tile prefixes (the per-tile tensor indices
+    // are functions of them), so a call on a resident table hashes ~n * 170 bytes and builds
+    // nothing else.
     uint64_t h = table_hash(descs.data(), n * sizeof(Desc), 0x243F6A8885A308D3ull ^ (uint64_t)mode);
     h = table_hash(start.data(), (n + 1) * sizeof(uint32_t), h);
     h = table_hash(&total, 8, h);
+    if (passes) h = table_hash(start2.data(), (n + 1) * sizeof(uint32_t), h);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!(flags & PGQ_TABLE_RESIDENT)) {
         std::vector<uint64_t> buf8((need + 7) / 8, 0);
         uint8_t* buf = reinterpret_cast<uint8_t*>(buf8.data());
         TableHeader* hdr = reinterpret_cast<TableHeader*>(buf);
-        memcpy(buf + desc_off, descs.data(), n * sizeof(Desc));
-        memcpy(buf + start_off, start.data(), (n + 1) * sizeof(uint32_t));
-        uint32_t* tdesc = reinterpret_cast<uint32_t*>(buf + tdesc_off);
+        memcpy(buf + L.desc_off, descs.data(), n * sizeof(Desc));
+        memcpy(buf + L.start_off, start.data(), (n + 1) * sizeof(uint32_t));
+        uint32_t* tdesc = reinterpret_cast<uint32_t*>(buf + L.tdesc_off);
         for (size_t i = 0; i < n; ++i)
             for (uint32_t t = start[i]; t < start[i + 1]; ++t) tdesc[t] = (uint32_t)i;
+        if (passes) {
+            memcpy(buf + L.start2_off, start2.data(), (n + 1) * sizeof(uint32_t));
+            uint32_t* tdesc2 = reinterpret_cast<uint32_t*>(buf + L.tdesc2_off);
+            for (size_t i = 0; i < n; ++i)                 // the TStates start at zero
+                for (uint32_t t = start2[i]; t < start2[i + 1]; ++t) tdesc2[t] = (uint32_t)i;
+        }
         hdr->magic = kTableMagic;
         hdr->checksum = h;
         hdr->n_desc = (uint32_t)n;
@@ -302,24 +345,47 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
         const hipError_t e = hipMemcpyAsync(ws, buf, need, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return hip_failed(e);
     }
+    const uint8_t* base = static_cast<const uint8_t*>(ws);
     KArgs ka;
     memset(&ka, 0, sizeof(ka));
-    ka.hdr = static_cast<const TableHeader*>(ws);
-    ka.table = reinterpret_cast<const Desc*>(static_cast<const uint8_t*>(ws) + desc_off);
-    ka.tile_start = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(ws) + start_off);
-    ka.tile_desc = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(ws) + tdesc_off);
+    ka.hdr = reinterpret_cast<const TableHeader*>(base);
+    ka.table = reinterpret_cast<const Desc*>(base + L.desc_off);
     ka.checksum = h;
     ka.status = dev_status;
-    ka.n_tiles = (uint32_t)total;
     ka.sqwa_k = sqwa_k;
     ka.fq_mode = fq_mode;
     ka.avg_init = avg_init;
     ka.avg_d = avg_d;
     ka.avg_c = avg_c;
+    void *ev_start = nullptr, *ev_stop = nullptr;
+    take_timing_events(&ev_start, &ev_stop);
+    // the whole-tensor clip select: one launch per digit and the final pick, then the main launch
+    if (passes) {
+        uint32_t feats2 = 0;
+        for (const Desc& d : descs)
+            if (d.flags & DF_TENSOR) feats2 |= features_avg(d);
+        KArgs k2 = ka;
+        k2.tile_start = reinterpret_cast<const uint32_t*>(base + L.start2_off);
+        k2.tile_desc = reinterpret_cast<const uint32_t*>(base + L.tdesc2_off);
+        k2.n_tiles = (uint32_t)total2;
+        k2.tsel_group = (int32_t)kSelGroup;
+        const uint32_t grid2 = grid_for(MODE_TSEL, feats2, true, k2.n_tiles);
+        for (int p = 0; p < passes; ++p) {
+            k2.tsel_pass = p;
+            set_timing_events(p == 0 ? ev_start : nullptr, nullptr);
+            if (const int e = launch(MODE_TSEL, feats2, k2, nullptr, grid2, stream)) return hip_failed((hipError_t)e);
+        }
+        if (const int e = launch_tensor_pick(k2, (uint32_t)n, stream)) return hip_failed((hipError_t)e);
+        ev_start = nullptr;
+    }
+    ka.tile_start = reinterpret_cast<const uint32_t*>(base + L.start_off);
+    ka.tile_desc = reinterpret_cast<const uint32_t*>(base + L.tdesc_off);
+    ka.n_tiles = (uint32_t)total;
     const bool averaging = mode == MODE_EMA || mode == MODE_SWA;
     uint32_t feats = 0;
     for (const Desc& d : descs) feats |= averaging ? features_avg(d) : features_of(d);
     const uint32_t grid = grid_for(mode, feats, true, ka.n_tiles);
+    set_timing_events(ev_start, ev_stop);
     if (const int e = launch(mode, feats, ka, nullptr, grid, stream)) return hip_failed((hipError_t)e);
     if (const hipError_t e = hipGetLastError()) return hip_failed(e);
     return PGQ_OK;
@@ -393,6 +459,7 @@ pgq_status check_plan_entry(const pgq_tensor_plan& p)
 {
     if (p.kind == PGQ_KIND_F16) return PGQ_OK;
     if (p.kind < 2 || p.kind > 8 || p.qp.bits != p.kind || !qparams_ok(p.qp)) return PGQ_ERR_PARAM;
+    if (p.per_tensor != 0 && p.per_tensor != 1) return PGQ_ERR_PARAM;
     return PGQ_OK;
 }
 
@@ -416,7 +483,14 @@ pgq_status export_desc(const pgq_tensor_in& t, const pgq_tensor_plan& p, uint8_t
     } else {
         d.kind = p.kind;
         d.Q = (1 << (p.kind - 1)) - 1;
-        d.rank_top = rank_top(t.cols, p.qp.pct_num, p.qp.pct_den);
+        if (p.per_tensor) {
+            if (p.has_awq) return PGQ_ERR_PARAM;
+            d.flags |= DF_TENSOR;
+            if (numel >= (int64_t(1) << 32)) return PGQ_ERR_SHAPE;
+            d.rank_top = numel > 0 ? rank_top(numel, p.qp.pct_num, p.qp.pct_den) : 1;
+        } else {
+            d.rank_top = rank_top(t.cols, p.qp.pct_num, p.qp.pct_den);
+        }
         if (arena && numel > 0) {
             if (p.codes_off < 0 || p.scales_off < 0) return PGQ_ERR_PARAM;
             d.codes = reinterpret_cast<int8_t*>(arena + p.codes_off);
@@ -583,6 +657,7 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
     if (pol->n_patterns < 0 || (pol->n_patterns > 0 && !pol->int8_patterns)) return PGQ_ERR_PARAM;
     if (!qparams_ok(pol->q_default) || !qparams_ok(pol->q_sensitive) || pol->passthrough_below < 0)
         return PGQ_ERR_PARAM;
+    if (pol->per_tensor != 0 && pol->per_tensor != 1) return PGQ_ERR_PARAM;
     int64_t off = 0;
     uint64_t nt = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -603,10 +678,13 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
             p.qp = sens ? pol->q_sensitive : pol->q_default;
             p.kind = p.qp.bits;
             p.has_awq = (!sens && x.awq_s) ? 1 : 0;
+            p.per_tensor = pol->per_tensor ? 1 : 0;
+            if (p.per_tensor && p.has_awq) return PGQ_ERR_PARAM;
+            if (p.per_tensor && numel >= (int64_t(1) << 32)) return PGQ_ERR_SHAPE;
             p.codes_off = off;
             off = align_up(off + numel, 256);
             p.scales_off = off;
-            off = align_up(off + x.rows * 2, 256);
+            off = align_up(off + (p.per_tensor ? 1 : x.rows) * 2, 256);
             if (p.has_awq) {
                 p.awq_off = off;
                 off = align_up(off + x.cols * 2, 256);
@@ -659,6 +737,7 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
         if (st != PGQ_OK) return st;
         st = check_plan_entry(plan[i]);
         if (st != PGQ_OK) return st;
+        if (plan[i].kind != PGQ_KIND_F16 && plan[i].per_tensor) return PGQ_ERR_PARAM;
         st = export_desc(snap[i], plan[i], nullptr, descs[i]);
         if (st != PGQ_OK) return st;
         if (snap[i].rows > 0 && snap[i].cols > 0) {

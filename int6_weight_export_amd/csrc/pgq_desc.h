@@ -14,11 +14,17 @@ constexpr int kWaves = 4;                 // wavefronts per workgroup
 constexpr int kBlock = 64 * kWaves;       // threads per workgroup
 constexpr uint64_t kTableMagic = 0x5047515441424c31ull;   // "PGQTABL1"
 
-enum Mode : int32_t { MODE_EXPORT = 0, MODE_SQWA = 1, MODE_FQ = 2, MODE_FQ_BWD = 3, MODE_EMA = 4, MODE_SWA = 5 };
-constexpr int kModes = 6;
+enum Mode : int32_t {
+    MODE_EXPORT = 0, MODE_SQWA = 1, MODE_FQ = 2, MODE_FQ_BWD = 3, MODE_EMA = 4, MODE_SWA = 5,
+    MODE_TSEL = 6     // one pass of the whole-tensor clip select (per-tensor scales)
+};
+constexpr int kModes = 7;
 enum : int32_t { IN_F32 = 0, IN_BF16 = 1 };
 enum : int32_t { KIND_F16 = 16 };
-enum : uint32_t { DF_VEC = 1u };          // 16-byte vector path allowed for this tensor
+enum : uint32_t {
+    DF_VEC = 1u,          // 16-byte vector path allowed for this tensor
+    DF_TENSOR = 2u        // one scale for the whole tensor, clip from its TState
+};
 
 // Features a launch needs; each kernel instantiation covers a fixed set of them, and the
 // host launches the leanest one that covers what its tensors need (fewer paths compiled
@@ -34,6 +40,18 @@ enum : uint32_t {
     F_ALL = 127u
 };
 
+// State of one tensor's whole-tensor clip select, in the caller's workspace.  Pass p of the
+// radix select adds every workgroup's LDS histogram of key digit p (bits 30..23, 22..15, 14..7,
+// 6..0 of |x|, among the keys matching the digits already chosen) into hist[p]; the digits
+// chosen so far are re-derived from hist[0 .. p-1] by whoever needs them.  The final pick
+// stores the selected key and zeroes hist / kmax, so consecutive calls need no reset.
+struct alignas(64) TState {
+    uint32_t hist[4][256];
+    uint32_t kmax;        // absmax select: running maximum key
+    uint32_t key;         // the selected |x| bit pattern, read by the quantize pass
+    uint32_t pad[14];
+};
+
 struct alignas(16) Desc {
     const void* w;            // input rows (fp32 or bf16), row stride ld elements
     int8_t* codes;            // rows x cols, dense
@@ -46,6 +64,7 @@ struct alignas(16) Desc {
     const uint16_t* grad;     // STE backward input (bf16, dense)
     uint16_t* grad_out;       // STE backward output (bf16, dense)
     uint8_t* mask;            // STE mask bits, rows x ceil(cols/8)
+    TState* tstate;           // DF_TENSOR: the tensor's select state (workspace)
     int64_t rows, cols, ld;
     int64_t rank_top;         // the clip is the rank_top-th largest |x| of the row (1 = max)
     int32_t kind;             // code bits, or KIND_F16
@@ -79,6 +98,8 @@ struct KArgs {
     int32_t avg_init;             // EMA: nonzero starts the average at the weights
     float avg_d;                  // EMA: decay d
     float avg_c;                  // EMA: fl32(1 - d)
+    int32_t tsel_pass;            // MODE_TSEL: 0 .. 3 (digits of bits 30..23, 22..15, 14..7, 6..0)
+    int32_t tsel_group;           // MODE_TSEL: export tiles per select tile
     int32_t reserved;
 };
 
@@ -89,8 +110,12 @@ struct KArgs {
 uint32_t variant_of(int mode, uint32_t need);
 int launch(int mode, uint32_t need, const KArgs& ka, const Desc* single, uint32_t grid, void* stream);
 int max_resident_blocks(int mode, uint32_t need, bool table, int* per_cu, int* n_cu);
-// The next launch on this host thread records these hipEvent_t at kernel start / end.
+// The next launch on this host thread records these hipEvent_t at kernel start / end (either
+// may be null); take_timing_events() hands back and clears a pending pair.
 void set_timing_events(void* start, void* stop);
+void take_timing_events(void** start, void** stop);
+// The final pick of the whole-tensor selects: one workgroup per descriptor.
+int launch_tensor_pick(const KArgs& ka, uint32_t n_desc, void* stream);
 
 // Register tile: a row of up to 64 * chunks * elements stays in VGPRs; longer rows stream.
 constexpr int64_t kRegCols_F32 = 64 * 8 * 4;     // 2048

@@ -218,6 +218,43 @@ __device__ __forceinline__ void load_u16(const GLB uint16_t* base, uint32_t e, u
 
 // ---- the clip: the r-th largest magnitude key of the row (keys = |x| bit patterns) -------------
 // `each(f)` calls f(key, valid) for every element slot this lane owns.
+// One wave over a 256-bin digit histogram: the bin holding the rem-th largest key (bins count
+// keys by digit, the largest digit last) and the number of keys in the bins above it.  All
+// lanes active; results uniform.
+// h: this lane's bins 4 lane .. 4 lane + 3.
+__device__ __forceinline__ void radix_digit_bins(const uint32_t (&h)[4], uint32_t rem, int lane, uint32_t& digit,
+                                                 uint32_t& above)
+{
+    const uint32_t s = h[0] + h[1] + h[2] + h[3];
+    uint32_t inc = s;                       // sum over lanes >= lane
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_down((int)inc, off, 64);
+        if (lane + off < 64) inc += v;
+    }
+    uint32_t run = inc - s;                 // count of keys in the bins above this lane's bins
+    int found = -1;
+    uint32_t abv = 0;
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+        if (found < 0 && run < rem && run + h[b] >= rem) { found = 4 * lane + b; abv = run; }
+        run += h[b];
+    }
+    const uint64_t bal = __ballot(found >= 0);
+    const int src = bal ? __ffsll((unsigned long long)bal) - 1 : 0;
+    digit = (uint32_t)__shfl(found, src, 64);
+    above = (uint32_t)__shfl((int)abv, src, 64);
+}
+
+template <class HistPtr>
+__device__ __forceinline__ void radix_digit(HistPtr hist, uint32_t rem, int lane, uint32_t& digit, uint32_t& above)
+{
+    uint32_t h[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) h[b] = hist[4 * lane + b];
+    radix_digit_bins(h, rem, lane, digit, above);
+}
+
 // The k-th largest (1 <= k <= 64) of the 64 values the lanes hold: a lane whose value has fewer
 // than k values above it and at least k at or above it holds the answer.  All lanes active.
 __device__ __forceinline__ uint32_t rank_select64(uint32_t v, uint32_t k)
@@ -297,30 +334,11 @@ __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t
             if (ok && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xFFu], 1u);
         });
         lds_sync_wave();
-        uint32_t h[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) h[b] = hist[4 * lane + b];
+        uint32_t digit, above;
+        radix_digit(hist, rem, lane, digit, above);
         lds_sync_wave();
-        const uint32_t s = h[0] + h[1] + h[2] + h[3];
-        uint32_t inc = s;                       // sum over lanes >= lane
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = (uint32_t)__shfl_down((int)inc, off, 64);
-            if (lane + off < 64) inc += v;
-        }
-        uint32_t run = inc - s;                 // count of keys in the bins above this lane's bins
-        int found = -1;
-        uint32_t above = 0;
-#pragma unroll
-        for (int b = 3; b >= 0; --b) {
-            if (found < 0 && run < rem && run + h[b] >= rem) { found = 4 * lane + b; above = run; }
-            run += h[b];
-        }
-        const uint64_t bal = __ballot(found >= 0);
-        const int src = bal ? __ffsll((unsigned long long)bal) - 1 : 0;
-        const int digit = __shfl(found, src, 64);
-        rem -= (uint32_t)__shfl((int)above, src, 64);
-        prefix |= (uint32_t)digit << shift;
+        rem -= above;
+        prefix |= digit << shift;
         pmask |= 0xFFu << shift;
     }
     return prefix & 0x7FFFFFFFu;
@@ -666,32 +684,37 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         for (int r = 0; r < R; ++r) {
             if (r < nrows) {
                 const int64_t row = row0 + r;
-                uint32_t mx = 0;
+                uint32_t ck;
+                if (d.flags & DF_TENSOR) {
+                    ck = gp(d.tstate)->key;         // the whole-tensor clip, selected beforehand
+                } else {
+                    uint32_t mx = 0;
 #pragma unroll
-                for (int i = 0; i < NCH; ++i)
-                    if (EXACT || 64 * i < nchunk)
+                    for (int i = 0; i < NCH; ++i)
+                        if (EXACT || 64 * i < nchunk)
 #pragma unroll
-                        for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[r][i][v]) & 0x7FFFFFFFu);   // padding is +0
-                mx = wave_max(mx);
-                if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
-                uint32_t ck = mx;
-                if constexpr (SEL) {
-                    if (d.rank_top > 1) {
-                        auto each = [&](auto&& f) {
+                            for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[r][i][v]) & 0x7FFFFFFFu);   // padding is +0
+                    mx = wave_max(mx);
+                    if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
+                    ck = mx;
+                    if constexpr (SEL) {
+                        if (d.rank_top > 1) {
+                            auto each = [&](auto&& f) {
 #pragma unroll
-                            for (int i = 0; i < NCH; ++i)
-                                if (EXACT || 64 * i < nchunk) {
-                                    const bool ok = (EXACT && i < NCH - 1) || lane + 64 * i < nchunk;
+                                for (int i = 0; i < NCH; ++i)
+                                    if (EXACT || 64 * i < nchunk) {
+                                        const bool ok = (EXACT && i < NCH - 1) || lane + 64 * i < nchunk;
 #pragma unroll
-                                    for (int v = 0; v < VEC; ++v) f(fbits(x[r][i][v]) & 0x7FFFFFFFu, ok);
-                                }
-                        };
-                        ck = kth_largest(each, d.rank_top, hist, lane);
+                                        for (int v = 0; v < VEC; ++v) f(fbits(x[r][i][v]) & 0x7FFFFFFFu, ok);
+                                    }
+                            };
+                            ck = kth_largest(each, d.rank_top, hist, lane);
+                        }
                     }
                 }
                 uint16_t s16;
                 set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
-                if (lane == 0 && d.scales) gp(d.scales)[row] = s16;
+                if (lane == 0 && d.scales && (row == 0 || !(d.flags & DF_TENSOR))) gp(d.scales)[row] = s16;
                 const RowOut ro = row_out(d, row);
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
@@ -729,21 +752,27 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 for (int v = 0; v < VEC; ++v) { a[v] = 1.0f; ainv[v] = 1.0f; }
             }
         };
-        uint32_t mx = 0;
-        for (int base = 0; base < nchunk; base += 64) {
-            const uint32_t c = (uint32_t)(base + lane);
-            if ((int)c < nchunk) {
-                float x[VEC], a[VEC], ainv[VEC];
-                load_chunk((uint32_t)base, x, a, ainv, a_out);
+        uint32_t ck = 0;
+        const bool tensor = (d.flags & DF_TENSOR) != 0;
+        if (tensor) {
+            ck = gp(d.tstate)->key;                 // the whole-tensor clip, selected beforehand
+        } else {
+            uint32_t mx = 0;
+            for (int base = 0; base < nchunk; base += 64) {
+                const uint32_t c = (uint32_t)(base + lane);
+                if ((int)c < nchunk) {
+                    float x[VEC], a[VEC], ainv[VEC];
+                    load_chunk((uint32_t)base, x, a, ainv, a_out);
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[v]) & 0x7FFFFFFFu);
+                    for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[v]) & 0x7FFFFFFFu);
+                }
             }
+            mx = wave_max(mx);
+            if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
+            ck = mx;
         }
-        mx = wave_max(mx);
-        if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
-        uint32_t ck = mx;
         if constexpr (SEL) {
-            if (d.rank_top > 1) {
+            if (!tensor && d.rank_top > 1) {
                 // f runs in uniform control flow (lanes past the row pass ok = false)
                 auto each = [&](auto&& f) {
                     for (int base = 0; base < nchunk; base += 64) {
@@ -764,7 +793,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         }
         uint16_t s16;
         set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
-        if (lane == 0 && d.scales) gp(d.scales)[row] = s16;
+        if (lane == 0 && d.scales && (row == 0 || !tensor)) gp(d.scales)[row] = s16;
         for (int base = 0; base < nchunk; base += 64) {
             const uint32_t c = (uint32_t)(base + lane);
             const bool ok = (int)c < nchunk;
@@ -1060,12 +1089,125 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nr
     }
 }
 
+// ---- whole-tensor clip select (per-tensor scales) ---------------------------------------------
+// The clip of a DF_TENSOR tensor is the rank_top-th largest |x| over all its elements
+// ("per-row / per-tensor quantization" with percentile clipping, PR #2159 Key Explored
+// Modifications), found by a radix select over the key bits 30..23, 22..15, 14..7, 6..0, one
+// launch per digit: every workgroup histograms the digits of its keys that match the digits
+// chosen so far in LDS and adds the histogram into hist[pass] with device atomics.  The chosen
+// digits are re-derived from the earlier passes' histograms at the start of each pass (the
+// launch boundary makes them complete), so no workgroup waits on another and none needs a
+// device-scope fence (on this chip that writes back and invalidates the XCD's L2).
+// pgq_tensor_pick_kernel finishes.  rank_top = 1 is a single max pass.
+
+// Digits 0 .. npass-1 of the select from a TState's histograms: the key prefix, its mask and
+// the rank still to find among the keys that match it.  One wave, all lanes; uniform results.
+__device__ __forceinline__ void tensor_prefix(const GLB TState* S, uint32_t rank, int npass, int lane,
+                                              uint32_t& prefix, uint32_t& pmask, uint32_t& rem)
+{
+    prefix = 0;
+    pmask = 0;
+    rem = rank;
+    uint32_t h[4][4];                               // every histogram's bins in one load round
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        if (p < npass) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) h[p][b] = S->hist[p][4 * lane + b];
+        }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        if (p < npass) {
+            const int shift = p == 0 ? 23 : p == 1 ? 15 : p == 2 ? 7 : 0;
+            uint32_t digit, above;
+            radix_digit_bins(h[p], rem, lane, digit, above);
+            rem -= above;
+            prefix |= digit << shift;
+            pmask |= 0xFFu << shift;
+        }
+    }
+}
+
+// One pass over rows [row0, row0 + nrows) of the tensor.  Whole workgroup; wg_hist: kWaves x 256
+// words of LDS.
+template <int IN, int VEC>
+__device__ __forceinline__ void tile_tensor_select(const Desc& d, int64_t row0, int64_t nrows, int wave, int lane,
+                                                   uint32_t* wg_hist, const KArgs& ka, uint32_t& st)
+{
+    TState* S = d.tstate;
+    const int pass = ka.tsel_pass;
+    const bool absmax = d.rank_top == 1;
+    if (absmax && pass > 0) return;                  // uniform: nothing left to select
+    const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+    uint32_t prefix, pmask, rem;
+    tensor_prefix(gp(S), (uint32_t)d.rank_top, absmax ? 0 : pass, lane, prefix, pmask, rem);
+    const int tid = (int)threadIdx.x;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wg_hist[256 * w + tid] = 0;   // one histogram per wave
+    __syncthreads();
+    uint32_t* my_hist = wg_hist + 256 * wave;       // waves do not contend for bins
+    const int nchunk = (int)(d.cols / VEC);
+    const size_t esz = IN == IN_F32 ? 4 : 2;
+    const int64_t rend = min(row0 + nrows, d.rows);
+    uint32_t m = 0, bad = 0;
+    for (int64_t row = row0 + wave; row < rend; row += kWaves) {
+        const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
+        for (int base = 0; base < nchunk; base += 64) {
+            const int c = base + lane;
+            if (c < nchunk) {
+                float x[VEC];
+                load_x<IN, VEC>(wrow, (uint32_t)c * VEC, x);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    const uint32_t k = fbits(x[v]) & 0x7FFFFFFFu;
+                    bad |= k >= 0x7F800000u ? 1u : 0u;
+                    if (absmax) m = max(m, k);
+                    else if ((k & pmask) == prefix) atomicAdd(&my_hist[(k >> shift) & 0xFFu], 1u);
+                }
+            }
+        }
+    }
+    if (pass == 0 && bad) st |= PGQ_DEV_NONFINITE;
+    if (absmax) {
+        m = wave_max(m);
+        if (lane == 0) wg_hist[wave] = m;           // absmax builds no histogram
+    }
+    __syncthreads();
+    if (absmax) {
+        if (tid == 0) atomicMax(&S->kmax, max(max(wg_hist[0], wg_hist[1]), max(wg_hist[2], wg_hist[3])));
+    } else {
+        const uint32_t c = wg_hist[tid] + wg_hist[256 + tid] + wg_hist[512 + tid] + wg_hist[768 + tid];
+        if (c) atomicAdd(&S->hist[pass][tid], c);
+    }
+}
+
 // A tile is tile_rows consecutive rows of one tensor; wave w takes groups of rgroup rows,
 // groups interleaved over the four waves.
 template <int MODE, uint32_t F>
 __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, int lane, uint32_t* hist,
                                         float* awq_lds, const KArgs& ka, uint32_t& st)
 {
+    if constexpr (MODE == MODE_TSEL) {
+        uint32_t* wg_hist = hist - 256 * wave;      // the workgroup's LDS histograms, 4 x 256 words
+        const int64_t nrows = (int64_t)d.tile_rows * ka.tsel_group;   // row0 counts select tiles
+        const bool vec = (d.flags & DF_VEC) != 0;
+        if constexpr ((F & F_F32) != 0) {
+            if (d.in_dtype == IN_F32) {
+                if constexpr ((F & F_SCALAR) != 0) {
+                    if (!vec) { tile_tensor_select<IN_F32, 1>(d, row0, nrows, wave, lane, wg_hist, ka, st); return; }
+                }
+                tile_tensor_select<IN_F32, 4>(d, row0, nrows, wave, lane, wg_hist, ka, st);
+                return;
+            }
+        }
+        if constexpr ((F & F_BF16) != 0) {
+            if constexpr ((F & F_SCALAR) != 0) {
+                if (!vec) { tile_tensor_select<IN_BF16, 1>(d, row0, nrows, wave, lane, wg_hist, ka, st); return; }
+            }
+            tile_tensor_select<IN_BF16, 8>(d, row0, nrows, wave, lane, wg_hist, ka, st);
+        }
+        return;
+    }
     // AWQ multipliers for the whole tile, once (rows that fit the register tile read them from
     // LDS).  The condition is uniform over the workgroup, so every wave reaches the barriers.
     const float* lds = nullptr;
@@ -1106,6 +1248,8 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
                  "s"(d.tile_rows), "s"(d.nch), "s"(d.w), "s"(d.Q));
     if constexpr (MODE == MODE_EXPORT) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.dq_dtype));
     if constexpr (MODE == MODE_SQWA || MODE == MODE_EMA || MODE == MODE_SWA) asm volatile("" ::"s"(d.mean));
+    if constexpr (MODE == MODE_TSEL) asm volatile("" ::"s"(d.tstate), "s"(d.rank_top), "s"(d.in_dtype));
+    if constexpr (MODE == MODE_EXPORT) asm volatile("" ::"s"(d.tstate));
     if constexpr (MODE == MODE_FQ || MODE == MODE_FQ_BWD)
         asm volatile("" ::"s"(d.dq), "s"(d.scales), "s"(d.mask), "s"(d.grad), "s"(d.grad_out));
     if constexpr ((F & F_PASS) != 0 && MODE == MODE_EXPORT) asm volatile("" ::"s"(d.f16_out));
@@ -1153,12 +1297,42 @@ pgq_table_kernel(const TableHeader* __restrict__ hdr,
         const uint32_t ndi = next < ka.n_tiles ? tile_desc[next] : 0;
         const uint32_t first = tile_start[di];
         const Desc d = fetch_desc<MODE, F>(table + di);
-        do_tile<MODE, F>(d, (int64_t)(tile - first) * d.tile_rows, wave, lane, hist, awq_lds, ka, st);
+        const int64_t trows = (int64_t)d.tile_rows * (MODE == MODE_TSEL ? ka.tsel_group : 1);
+        do_tile<MODE, F>(d, (int64_t)(tile - first) * trows, wave, lane, hist, awq_lds, ka, st);
         tile = next;
         di = ndi;
     }
     st = wave_or(st);
     if (st && lane == 0 && ka.status) atomicOr(ka.status, st);
+}
+
+// Final pick of the whole-tensor selects: workgroup i, when tensor i has a per-tensor scale,
+// derives its last digit from the histograms (or takes the absmax), stores the key for the
+// quantize pass and zeroes the histograms and the running max for the next call.
+__global__ void __launch_bounds__(kBlock) pgq_tensor_pick_kernel(const TableHeader* __restrict__ hdr,
+                                                                const Desc* __restrict__ table, KArgs ka)
+{
+    if (hdr->magic != kTableMagic || hdr->checksum != ka.checksum) return;   // the select pass reported it
+    if (blockIdx.x >= hdr->n_desc) return;
+    const Desc* dp = table + blockIdx.x;
+    if (!(dp->flags & DF_TENSOR) || dp->rows <= 0 || dp->cols <= 0) return;
+    GLB TState* S = gp(dp->tstate);
+    const int tid = (int)threadIdx.x;
+    if (dp->rank_top == 1) {                        // absmax: one pass
+        if (tid == 0) {
+            S->key = S->kmax;
+            S->kmax = 0;
+        }
+        return;
+    }
+    if (tid < 64) {
+        uint32_t prefix, pmask, rem;
+        tensor_prefix(S, (uint32_t)dp->rank_top, 4, tid, prefix, pmask, rem);
+        if (tid == 0) S->key = prefix & 0x7FFFFFFFu;
+    }
+    __syncthreads();                                // the histograms are read before they are cleared
+#pragma unroll
+    for (int p = 0; p < 4; ++p) S->hist[p][tid] = 0;
 }
 
 // Single-matrix launches: the descriptor is a kernel argument.
@@ -1188,10 +1362,10 @@ const void* kernel_ptr(bool table)
 constexpr uint32_t kExportVariants[] = {F_F32 | F_PASS, F_BF16 | F_PASS, F_F32 | F_PASS | F_AWQ,
                                         F_F32 | F_PASS | F_SEL, F_ALL};
 constexpr uint32_t kFqVariants[] = {F_BF16, F_BF16 | F_SEL, F_ALL};
-constexpr uint32_t kAvgAll = F_F32 | F_BF16 | F_SCALAR;
+constexpr uint32_t kAvgAll = F_F32 | F_BF16 | F_SCALAR;   // also the whole-tensor select's
 constexpr uint32_t kAvgVariants[] = {F_F32, F_BF16, kAvgAll};
 
-// Weight averaging runs as grouped launches only.
+// Weight averaging and the whole-tensor select run as grouped launches only.
 template <int MODE>
 const void* average_kernel(uint32_t v, bool table)
 {
@@ -1227,6 +1401,7 @@ const void* pick(int mode, uint32_t need, bool table)
         return kernel_ptr<MODE_FQ, F_ALL>(table);
     case MODE_FQ_BWD: return kernel_ptr<MODE_FQ_BWD, F_ALL>(table);
     case MODE_EMA: return average_kernel<MODE_EMA>(v, table);
+    case MODE_TSEL: return average_kernel<MODE_TSEL>(v, table);
     case MODE_SWA: return average_kernel<MODE_SWA>(v, table);
     default: return nullptr;
     }
@@ -1242,7 +1417,7 @@ uint32_t variant_of(int mode, uint32_t need)
     } else if (mode == MODE_FQ) {
         for (uint32_t v : kFqVariants)
             if ((need & ~v) == 0) return v;
-    } else if (mode == MODE_EMA || mode == MODE_SWA) {
+    } else if (mode == MODE_EMA || mode == MODE_SWA || mode == MODE_TSEL) {
         for (uint32_t v : kAvgVariants)
             if ((need & ~v) == 0) return v;
         return kAvgAll;
@@ -1264,6 +1439,24 @@ hipError_t launch_args(const void* fn, uint32_t grid, void** args, hipStream_t s
     return hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, s);
 }
 }  // namespace
+
+int launch_tensor_pick(const KArgs& ka, uint32_t n_desc, void* stream)
+{
+    if (n_desc == 0) return (int)hipErrorInvalidValue;
+    KArgs copy = ka;
+    const TableHeader* hdr = ka.hdr;
+    const Desc* table = ka.table;
+    void* args[] = {&hdr, &table, &copy};
+    return (int)launch_args(reinterpret_cast<const void*>(&pgq_tensor_pick_kernel), n_desc, args,
+                            static_cast<hipStream_t>(stream));
+}
+
+void take_timing_events(void** start, void** stop)
+{
+    *start = t_start;
+    *stop = t_stop;
+    t_start = t_stop = nullptr;
+}
 
 void set_timing_events(void* start, void* stop)
 {

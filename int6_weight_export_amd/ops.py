@@ -158,10 +158,11 @@ def _tensor_in_array(tensors: Sequence[ExportTensor]):
 
 
 def make_policy(int8_patterns=DEFAULT_INT8_PATTERNS, passthrough_below: int = 65536,
-                q_default=(6, 9999, 10000), q_sensitive=(8, 1, 1)):
+                q_default=(6, 9999, 10000), q_sensitive=(8, 1, 1), per_tensor: bool = False):
     pats = [p.encode() for p in int8_patterns]
     parr = (ctypes.c_char_p * max(1, len(pats)))(*pats)
-    pol = pgq.pgq_policy(ctypes.cast(parr, ctypes.POINTER(ctypes.c_char_p)), len(pats), 0, passthrough_below,
+    pol = pgq.pgq_policy(ctypes.cast(parr, ctypes.POINTER(ctypes.c_char_p)), len(pats), 1 if per_tensor else 0,
+                         passthrough_below,
                          pgq.pgq_qparams(*q_default), pgq.pgq_qparams(*q_sensitive))
     pol._keep = (pats, parr)
     return pol
@@ -213,7 +214,8 @@ class Exporter:
                 rec["f16"] = self.arena[p.f16_off:p.f16_off + 2 * rows * cols].view(torch.int16).view(t.w.shape)
             else:
                 rec["codes"] = self.arena[p.codes_off:p.codes_off + rows * cols].view(torch.int8).view(rows, cols)
-                rec["scales"] = self.arena[p.scales_off:p.scales_off + 2 * rows].view(torch.int16)
+                ns = 1 if p.per_tensor else rows
+                rec["scales"] = self.arena[p.scales_off:p.scales_off + 2 * ns].view(torch.int16)
                 if p.has_awq:
                     rec["awq"] = self.arena[p.awq_off:p.awq_off + 2 * cols].view(torch.int16)
             if self.dq is not None:

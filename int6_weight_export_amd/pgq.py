@@ -64,13 +64,13 @@ class pgq_tensor_in(ctypes.Structure):
 
 class pgq_policy(ctypes.Structure):
     _fields_ = [("int8_patterns", ctypes.POINTER(ctypes.c_char_p)), ("n_patterns", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("passthrough_below", ctypes.c_int64),
+                ("per_tensor", ctypes.c_int32), ("passthrough_below", ctypes.c_int64),
                 ("q_default", pgq_qparams), ("q_sensitive", pgq_qparams)]
 
 
 class pgq_tensor_plan(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("has_awq", ctypes.c_int32), ("qp", pgq_qparams),
-                ("codes_off", ctypes.c_int64), ("scales_off", ctypes.c_int64),
+                ("per_tensor", ctypes.c_int32), ("codes_off", ctypes.c_int64), ("scales_off", ctypes.c_int64),
                 ("f16_off", ctypes.c_int64), ("awq_off", ctypes.c_int64)]
 
 

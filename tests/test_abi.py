@@ -204,3 +204,62 @@ def test_average_argument_errors():
     arr[1].awq_s = 0
     arr[3].dtype = 9
     assert swa(arr, 4, st, 2, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_DTYPE
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """ctypes mirrors of the header's structs have the C sizes and field offsets."""
+    import subprocess
+    structs = {"pgq_qparams": pgq.pgq_qparams, "pgq_fq_tensor": pgq.pgq_fq_tensor,
+               "pgq_tensor_in": pgq.pgq_tensor_in, "pgq_policy": pgq.pgq_policy,
+               "pgq_tensor_plan": pgq.pgq_tensor_plan}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(void) {']
+    for name, cls in structs.items():
+        lines.append(f'printf("{name} size %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines.append("return 0; }")
+    src, exe = tmp_path / "layout.c", tmp_path / "layout"
+    src.write_text("\n".join(lines))
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    for line in filter(None, out):
+        name, field, val = line.split()
+        cls = structs[name]
+        got = ctypes.sizeof(cls) if field == "size" else getattr(cls, field).offset
+        assert got == int(val), line
+
+
+def test_per_tensor_plan():
+    ts = synth.config2()[:8]
+    arr, keep = _tensor_array(ts)
+    pol, k2 = _policy()
+    pol.per_tensor = 1
+    plan = (pgq.pgq_tensor_plan * 8)()
+    ab, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert pgq.pgq_export_plan(arr, 8, ctypes.byref(pol), plan, ctypes.byref(ab), ctypes.byref(wb)) == 0
+    opol = oracle.Policy(per_tensor=True)
+    for i, t in enumerate(ts):
+        kind = oracle.tensor_kind(t.name, t.numel, opol)
+        if kind == oracle.KIND_F16:
+            assert plan[i].kind == pgq.PGQ_KIND_F16
+            continue
+        assert plan[i].kind == kind and plan[i].per_tensor == 1
+        assert plan[i].scales_off % 256 == 0
+        # the scales region holds one fp16: the next region starts 256 bytes later
+        nxt = [plan[j].codes_off for j in range(i + 1, 8) if plan[j].codes_off >= 0] + \
+              [plan[j].f16_off for j in range(i + 1, 8) if plan[j].f16_off >= 0]
+        if nxt:
+            assert min(nxt) == plan[i].scales_off + 256
+    # per-tensor scales do not combine with AWQ; the flag is 0 or 1; SQWA takes per-row plans only
+    arr_awq, keep2 = _tensor_array(synth.config4()[1:3], awq=True)
+    plan2 = (pgq.pgq_tensor_plan * 2)()
+    assert pgq.pgq_export_plan(arr_awq, 2, ctypes.byref(pol), plan2, ctypes.byref(ab),
+                               ctypes.byref(wb)) == pgq.PGQ_ERR_PARAM
+    pol.per_tensor = 2
+    assert pgq.pgq_export_plan(arr, 8, ctypes.byref(pol), plan, ctypes.byref(ab),
+                               ctypes.byref(wb)) == pgq.PGQ_ERR_PARAM
+    pol.per_tensor = 1
+    assert pgq.pgq_export_plan(arr, 8, ctypes.byref(pol), plan, ctypes.byref(ab), ctypes.byref(wb)) == 0
+    means = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    assert pgq.pgq_sqwa_accumulate(arr, 8, plan, means, 1, FAKE, wb.value, 0, None,
+                                   None) == pgq.PGQ_ERR_PARAM
