@@ -59,6 +59,12 @@ def load():
             lib.orc_quantize_rows.restype = _U32
             lib.orc_quantize_tensor.argtypes = [_P, _I64, _I64, _I64, _I32, _U32, _U32, _P, _P, _P, _P]
             lib.orc_quantize_tensor.restype = _U32
+            lib.orc_pack6_rows.argtypes = [_P, _I64, _I64, _P]
+            lib.orc_pack6_rows.restype = None
+            lib.orc_unpack6_rows.argtypes = [_P, _I64, _I64, _P]
+            lib.orc_unpack6_rows.restype = None
+            lib.orc_dequant_rows.argtypes = [_P, _I64, _I64, _P, _I32, _P, _P]
+            lib.orc_dequant_rows.restype = None
             lib.orc_awq_multipliers.argtypes = [_P, _I64, _P]
             lib.orc_awq_multipliers.restype = _U32
             lib.orc_fakequant_rows.argtypes = [_P, _I64, _I64, _I64, _I32, _U32, _U32, _P, _P, _P, _P, _P, _P]
@@ -211,3 +217,37 @@ def swa_update(mean: np.ndarray, w, k: int) -> int:
     w = np.ascontiguousarray(w, dtype=np.float32)
     assert w.size == mean.size
     return int(load().orc_swa_update(_ptr(mean), _ptr(w), mean.size, k))
+
+
+def pack6_row_bytes(cols: int) -> int:
+    return 3 * ((cols + 3) // 4)
+
+
+def pack6(codes) -> np.ndarray:
+    """int8 codes [rows, cols] in [-32, 31] -> packed bytes [rows, 3 * ceil(cols / 4)]."""
+    c = np.ascontiguousarray(codes, dtype=np.int8)
+    assert c.ndim == 2
+    rows, cols = c.shape
+    out = np.empty((rows, pack6_row_bytes(cols)), dtype=np.uint8)
+    load().orc_pack6_rows(_ptr(c), rows, cols, _ptr(out))
+    return out
+
+
+def unpack6(packed, cols: int) -> np.ndarray:
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    rows = p.shape[0]
+    assert p.shape == (rows, pack6_row_bytes(cols))
+    out = np.empty((rows, cols), dtype=np.int8)
+    load().orc_unpack6_rows(_ptr(p), rows, cols, _ptr(out))
+    return out
+
+
+def dequant(codes, scales, per_tensor: bool = False, awq=None) -> np.ndarray:
+    """x = code * s (/ a_j) for int8 codes [rows, cols] with fp16 scales (bit patterns)."""
+    c = np.ascontiguousarray(codes, dtype=np.int8)
+    rows, cols = c.shape
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    a = None if awq is None else np.ascontiguousarray(awq, dtype=np.uint16)
+    out = np.empty((rows, cols), dtype=np.float32)
+    load().orc_dequant_rows(_ptr(c), rows, cols, _ptr(s), 1 if per_tensor else 0, _ptr(a), _ptr(out))
+    return out

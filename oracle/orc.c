@@ -229,6 +229,59 @@ uint32_t orc_quantize_tensor(const float* w, int64_t rows, int64_t cols, int64_t
     return st;
 }
 
+/* 6-bit code storage (the "int6 artifact savings" of the PR #69 card's Novel Contributions; the
+ * pages give no byte layout).  Reading: each row's int6 codes, as 6-bit two's complement, four
+ * to three bytes, least significant bits first: group g holds codes 4g .. 4g+3 in the 24-bit
+ * little-endian word bytes[3g] | bytes[3g+1] << 8 | bytes[3g+2] << 16, code 4g + t in bits
+ * 6t .. 6t+5.  A row takes 3 * ceil(cols / 4) bytes; a short last group is padded with code 0. */
+int64_t orc_pack6_row_bytes(int64_t cols) { return 3 * ((cols + 3) / 4); }
+
+void orc_pack6_rows(const int8_t* codes, int64_t rows, int64_t cols, uint8_t* out)
+{
+    int64_t rb = orc_pack6_row_bytes(cols);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t g = 0; g < (cols + 3) / 4; ++g) {
+            uint32_t word = 0;
+            for (int t = 0; t < 4; ++t) {
+                int64_t j = 4 * g + t;
+                int32_t c = j < cols ? codes[r * cols + j] : 0;
+                word |= ((uint32_t)c & 0x3Fu) << (6 * t);
+            }
+            out[r * rb + 3 * g] = (uint8_t)(word & 0xFFu);
+            out[r * rb + 3 * g + 1] = (uint8_t)((word >> 8) & 0xFFu);
+            out[r * rb + 3 * g + 2] = (uint8_t)((word >> 16) & 0xFFu);
+        }
+    }
+}
+
+void orc_unpack6_rows(const uint8_t* in, int64_t rows, int64_t cols, int8_t* codes)
+{
+    int64_t rb = orc_pack6_row_bytes(cols);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j) {
+            int64_t g = j / 4;
+            uint32_t word = (uint32_t)in[r * rb + 3 * g] | ((uint32_t)in[r * rb + 3 * g + 1] << 8) |
+                            ((uint32_t)in[r * rb + 3 * g + 2] << 16);
+            int32_t f = (int32_t)((word >> (6 * (j % 4))) & 0x3Fu);
+            codes[r * cols + j] = (int8_t)(f >= 32 ? f - 64 : f);
+        }
+}
+
+/* Decode of stored codes (the dequant the export defines): x = code * s, divided by a_j when the
+ * tensor has AWQ multipliers; s = scales[r], or scales[0] for a per-tensor scale. */
+void orc_dequant_rows(const int8_t* codes, int64_t rows, int64_t cols, const uint16_t* scales, int32_t per_tensor,
+                      const uint16_t* awq, float* out)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        float s = orc_f16_to_f32(scales[per_tensor ? 0 : r]);
+        for (int64_t j = 0; j < cols; ++j) {
+            float d = (float)codes[r * cols + j] * s;
+            if (awq) d = d / orc_f16_to_f32(awq[j]);
+            out[r * cols + j] = d;
+        }
+    }
+}
+
 /* AWQ column multipliers a_j = fp16_rne(sqrt(s_j)) (exponent 1/2), s_j > 0 and finite. */
 uint32_t orc_awq_multipliers(const float* s, int64_t cols, uint16_t* a)
 {

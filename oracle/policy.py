@@ -42,6 +42,7 @@ class Policy:
     q6: Tuple[int, int, int] = (6, 9999, 10000)   # (bits, pct_num, pct_den)
     q8: Tuple[int, int, int] = (8, 1, 1)
     per_tensor: bool = False                      # one scale per integer-kind tensor
+    pack6: bool = False                           # int6 codes stored 4 per 3 bytes
 
 
 def qmax(bits: int) -> int:
@@ -102,6 +103,8 @@ def export(tensors, pol: Policy, awq: Optional[Dict[str, np.ndarray]] = None) ->
                 r = lib.quantize_rows(w.reshape(rows, cols), Q, num, den, awq=a)
             rec.update(codes=r["codes"], scales=r["scales"], dq=r["dq"].reshape(w.shape),
                        status=st | r["status"])
+            if pol.pack6 and kind == KIND_INT6:
+                rec["packed"] = lib.pack6(r["codes"])
         out.append(rec)
     return out
 
