@@ -92,9 +92,10 @@ def cpu_baseline(tensors, min_seconds: float = 10.0, max_passes: int = 30) -> di
 class Workload:
     """One bench workload: `step(i)` enqueues one step on input set i % copies."""
 
-    def __init__(self, name, desc, nbytes, rows, step, statuses, config, kernel):
+    def __init__(self, name, desc, nbytes, rows, step, statuses, config, kernel, launches=1, timed_calls=()):
         self.name, self.desc, self.nbytes, self.rows = name, desc, nbytes, rows
         self.step, self.statuses, self.config, self.kernel = step, statuses, config, kernel
+        self.launches, self.timed_calls = launches, list(timed_calls)   # library calls per step
 
 
 def _dev(a, torch):
@@ -220,7 +221,74 @@ def workload_sqwa(copies, torch, ops):
                        "fp32 running mean, then int6 codes + scales of the mean; 17 launches per step",
            "tensors": len(base), "params": int(numel), "snapshots": 16}
     return Workload("sqwa", cfg["workload"], nbytes, 17 * rows, step,
-                    lambda: [int(sq.status.item()), int(ex.status.item())], cfg, "pgq_table_kernel<1, 5u>"), None
+                    lambda: [int(sq.status.item()), int(ex.status.item())], cfg, "pgq_table_kernel<1, 5u>",
+                    launches=17, timed_calls=[(ops.Sqwa, "accumulate"), (ops.Exporter, "run")]), None
+
+
+def algorithmic_bytes_pack6(tensors) -> int:
+    """Export with 6-bit int6 codes: as algorithmic_bytes, with 3/4 byte per int6 code."""
+    import oracle
+
+    pol = oracle.Policy(pack6=True)
+    total = algorithmic_bytes(tensors, want_dq=True)["total"]
+    for t in tensors:
+        if oracle.tensor_kind(t.name, t.numel, pol) == oracle.KIND_INT6:
+            rows, cols = oracle.as_rows(t.shape)
+            total += rows * 3 * ((cols + 3) // 4) - t.numel
+    return total
+
+
+def workload_pack6(copies, torch, ops):
+    """The whole-model export with int6 codes stored four per three bytes."""
+    tensors = synth.config2()
+    sets = []
+    for _ in range(copies):
+        ex = ops.Exporter([ops.ExportTensor(t.name, _dev(t.data, torch)) for t in tensors],
+                          ops.make_policy(pack6=True), want_dq=True)
+        ex.run()
+        sets.append(ex)
+    cfg = {"workload": "whole-model export of the 9-layer d=512 GPT weight set with int6 codes stored four per "
+                       "three bytes (99.99th-percentile clip), int8 tok_emb.weight, fp16 vectors, fp32 dequant",
+           "tensors": len(tensors), "params": int(sum(t.numel for t in tensors))}
+    rows = algorithmic_bytes(tensors, want_dq=True)["rows"]
+    return Workload("pack6", cfg["workload"], algorithmic_bytes_pack6(tensors), rows,
+                    lambda i: sets[i % len(sets)].run(), lambda: [int(s.status.item()) for s in sets], cfg,
+                    "pgq_table_kernel<7, 5u>"), tensors
+
+
+def workload_decode(copies, torch, ops):
+    """Decode of the exported 9-layer artifact (6-bit int6 codes, int8 tok_emb, fp16 scales) back to
+    fp32 weights: one pgq_dequant_codes call per integer tensor."""
+    tensors = synth.config2()
+    sets = []
+    nbytes = rows = 0
+    for k in range(copies):
+        ex = ops.Exporter([ops.ExportTensor(t.name, _dev(t.data, torch)) for t in tensors],
+                          ops.make_policy(pack6=True), want_dq=False)
+        ex.run()
+        jobs = []
+        for t, o in zip(tensors, ex.outputs()):
+            if o["kind"] == 16:
+                continue
+            r, c = (t.shape[0], t.numel // t.shape[0])
+            packed = "packed" in o
+            codes = o["packed"] if packed else o["codes"]
+            out = torch.empty(r, c, dtype=torch.float32, device="cuda")
+            jobs.append((codes, o["scales"], c, packed, out))
+            if k == 0:
+                nbytes += codes.numel() + 2 * r + 4 * r * c
+                rows += r
+        sets.append(jobs)
+
+    def step(i):
+        for codes, scales, c, packed, out in sets[i % len(sets)]:
+            ops.dequant_codes(codes, scales, c, packed=packed, out=out)
+
+    cfg = {"workload": "decode of the exported 9-layer d=512 artifact (int6 codes four per three bytes, int8 "
+                       "tok_emb.weight, fp16 row scales) to fp32 weights, one call per tensor",
+           "tensors": len(sets[0]), "params": int(sum(t.numel for t in tensors if t.numel >= 65536))}
+    return Workload("decode", cfg["workload"], nbytes, rows, step, lambda: [0], cfg, "pgq_decode_kernel",
+                    launches=len(sets[0]), timed_calls=[(ops, "dequant_codes")]), None
 
 
 def workload_tensor(copies, torch, ops):
@@ -287,7 +355,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 1000; 50 for --mode sqwa)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 50; 3 for --mode sqwa)")
-    ap.add_argument("--mode", default="export", choices=["export", "awq", "batch", "select", "fakequant", "sqwa", "ema", "swa", "tensor"],
+    ap.add_argument("--mode", default="export", choices=["export", "awq", "batch", "select", "fakequant", "sqwa", "ema", "swa", "tensor",
+                                                    "pack6", "decode"],
                     help="export (default): the 9-layer whole-model export; the others time the remaining "
                          "rows of the path")
     ap.add_argument("--copies", type=int, default=6, help="input/output sets used in rotation")
@@ -300,7 +369,7 @@ def main() -> int:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer is "
               f"row-parallel within a GPU and this build runs no collectives)", file=sys.stderr)
         return 2
-    steps = args.steps if args.steps is not None else (50 if args.mode == "sqwa" else 1000)
+    steps = args.steps if args.steps is not None else {"sqwa": 50, "decode": 200}.get(args.mode, 1000)
     warmup = args.warmup if args.warmup is not None else (3 if args.mode == "sqwa" else 50)
 
     import torch
@@ -310,7 +379,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     make = {"export": workload_export, "awq": workload_awq, "batch": workload_batch, "select": workload_select,
-            "ema": workload_ema, "swa": workload_swa, "tensor": workload_tensor,
+            "ema": workload_ema, "swa": workload_swa, "tensor": workload_tensor, "pack6": workload_pack6,
+            "decode": workload_decode,
             "sqwa": workload_sqwa}
     if args.mode == "fakequant":
         wl, tensors = workload_fakequant(args.copies, torch, ops, pgq)
@@ -333,7 +403,7 @@ def main() -> int:
     # its dispatch (pgq_time_next_launch), so a pair times one kernel alone, on the stream it
     # runs on.  Recording them costs host time per launch, which is why the throughput steps
     # above run without them.
-    launches = 17 if args.mode == "sqwa" else 1
+    launches = wl.launches
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps * launches)]
     for a, b in ev:                              # create the underlying HIP events
@@ -342,22 +412,23 @@ def main() -> int:
     handles = [(ctypes.c_void_p(a.cuda_event), ctypes.c_void_p(b.cuda_event)) for a, b in ev]
     torch.cuda.synchronize()
     if launches > 1:
+        # every library call of a step gets its own event pair
         it = iter(handles)
-        orig = ops.Sqwa.accumulate, ops.Exporter.run
+        saved = [(obj, name, getattr(obj, name)) for obj, name in wl.timed_calls]
 
-        def acc(self, *a, **k):
-            pgq.pgq_time_next_launch(*next(it))
-            return orig[0](self, *a, **k)
-
-        def run(self, *a, **k):
-            pgq.pgq_time_next_launch(*next(it))
-            return orig[1](self, *a, **k)
-        ops.Sqwa.accumulate, ops.Exporter.run = acc, run
+        def timed(fn):
+            def call(*a, **k):
+                pgq.pgq_time_next_launch(*next(it))
+                return fn(*a, **k)
+            return call
+        for obj, name, fn in saved:
+            setattr(obj, name, timed(fn))
         try:
             for i in range(steps):
                 wl.step(i)
         finally:
-            ops.Sqwa.accumulate, ops.Exporter.run = orig
+            for obj, name, fn in saved:
+                setattr(obj, name, fn)
     else:
         for i in range(steps):
             pgq.pgq_time_next_launch(*handles[i])

@@ -169,6 +169,10 @@ typedef struct {
     int64_t passthrough_below;        /* tensors with fewer elements are stored as fp16 (65536) */
     pgq_qparams q_default;            /* e.g. {6, 9999, 10000} */
     pgq_qparams q_sensitive;          /* e.g. {8, 1, 1} */
+    int32_t pack6;                    /* 1: 6-bit tensors store their codes four per three bytes
+                                         (the int6 artifact savings of the PR #69 card; layout
+                                         below at pgq_dequant_codes) */
+    int32_t reserved;
 } pgq_policy;
 
 typedef struct {
@@ -180,13 +184,15 @@ typedef struct {
     int64_t scales_off;
     int64_t f16_off;
     int64_t awq_off;
+    int32_t packed;         /* 1: codes region holds 6-bit packed codes, 3 * ceil(cols / 4) bytes per row */
+    int32_t reserved;
 } pgq_tensor_plan;
 
 /* Host only (no device work): decide each tensor's kind and lay out the output arena.
  * plan: host array of n entries (written).  arena_bytes / workspace_bytes: sizes the
  * caller must allocate for pgq_export_model / pgq_sqwa_accumulate.  Regions are 256-byte
- * aligned: codes rows x cols int8, scales rows fp16 (1 when per_tensor), f16 numel fp16, awq
- * cols fp16.  PGQ_ERR_PARAM when per_tensor meets AWQ scales; PGQ_ERR_SHAPE when a per-tensor
+ * aligned: codes rows x cols int8 (packed: rows x 3 * ceil(cols / 4) bytes), scales rows fp16
+ * (1 when per_tensor), f16 numel fp16, awq cols fp16.  PGQ_ERR_PARAM when per_tensor meets AWQ scales; PGQ_ERR_SHAPE when a per-tensor
  * tensor has 2^32 elements or more. */
 pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* pol,
                            pgq_tensor_plan* plan, size_t* arena_bytes, size_t* workspace_bytes);
@@ -211,6 +217,22 @@ pgq_status pgq_export_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_
 pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_tensor_plan* plan,
                                float* const* mean, int32_t k, void* workspace, size_t workspace_bytes,
                                uint32_t flags, uint32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Decode stored codes back to fp32 weights (the artifact loader): x = code * s, divided by     */
+/* a_j when awq_mult is given -- bit for bit the dequantized value the export produced.        */
+/*   codes      device, rows x cols int8 (packed = 0) or rows x 3 * ceil(cols / 4) bytes        */
+/*              (packed = 1): per row, group g of three bytes is the little-endian 24-bit word  */
+/*              holding codes 4g .. 4g+3 as 6-bit two's complement fields, code 4g + t in bits  */
+/*              6t .. 6t+5; a short last group is padded with code 0                            */
+/*   scales     device fp16 bit patterns: rows of them, or one when per_tensor = 1              */
+/*   awq_mult   NULL, or device cols fp16 multipliers a_j (bit patterns, as exported)           */
+/*   out        device rows x cols fp32, dense                                                  */
+/* Reads and writes only; no status bits are produced (dev_status may be NULL).                */
+/* ------------------------------------------------------------------------------------------ */
+pgq_status pgq_dequant_codes(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,
+                             int32_t per_tensor, const uint16_t* awq_mult, float* out, uint32_t* dev_status,
+                             void* stream);
 
 /* ------------------------------------------------------------------------------------------ */
 /* Weight averaging without quantization, grouped over n tensors in one launch.               */

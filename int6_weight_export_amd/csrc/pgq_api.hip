@@ -116,7 +116,7 @@ void set_vec_flag(Desc& d)
     const size_t ein = d.in_dtype == IN_F32 ? 4 : 2;
     bool ok = d.cols % vec == 0 && d.ld % vec == 0 && aligned(d.w, 16);
     const size_t dqe = d.dq_dtype == IN_F32 ? 4 : 2;
-    ok = ok && (!d.codes || aligned(d.codes, vec));
+    ok = ok && (!d.codes || (d.flags & DF_PACK6) || aligned(d.codes, vec));
     ok = ok && (!d.dq || aligned(d.dq, std::min<size_t>(16, vec * dqe)));
     ok = ok && (!d.awq_s || aligned(d.awq_s, 16));
     ok = ok && (!d.awq_out || aligned(d.awq_out, vec * 2));
@@ -276,6 +276,9 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
                        uint32_t flags, uint32_t* dev_status, int sqwa_k, int fq_mode, void* stream,
                        int avg_init = 0, float avg_d = 0.0f, float avg_c = 0.0f)
 {
+    if (mode == MODE_EXPORT)
+        for (const Desc& d : descs_in)
+            if (d.flags & DF_PACK6) mode = MODE_EXPORT6;
     // Longest tiles first: workgroups start in tile order, so the launch ends on the shortest
     // tiles and its tail is short.  (The tensors' order has no other meaning to the kernel.)
     std::vector<Desc> descs(descs_in);
@@ -460,6 +463,7 @@ pgq_status check_plan_entry(const pgq_tensor_plan& p)
     if (p.kind == PGQ_KIND_F16) return PGQ_OK;
     if (p.kind < 2 || p.kind > 8 || p.qp.bits != p.kind || !qparams_ok(p.qp)) return PGQ_ERR_PARAM;
     if (p.per_tensor != 0 && p.per_tensor != 1) return PGQ_ERR_PARAM;
+    if (p.packed != 0 && (p.packed != 1 || p.kind != 6)) return PGQ_ERR_PARAM;
     return PGQ_OK;
 }
 
@@ -495,6 +499,7 @@ pgq_status export_desc(const pgq_tensor_in& t, const pgq_tensor_plan& p, uint8_t
             if (p.codes_off < 0 || p.scales_off < 0) return PGQ_ERR_PARAM;
             d.codes = reinterpret_cast<int8_t*>(arena + p.codes_off);
             d.scales = reinterpret_cast<uint16_t*>(arena + p.scales_off);
+            if (p.packed) d.flags |= DF_PACK6;
         }
         if (p.has_awq) {
             if (!t.awq_s) return PGQ_ERR_NULL;
@@ -658,6 +663,7 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
     if (!qparams_ok(pol->q_default) || !qparams_ok(pol->q_sensitive) || pol->passthrough_below < 0)
         return PGQ_ERR_PARAM;
     if (pol->per_tensor != 0 && pol->per_tensor != 1) return PGQ_ERR_PARAM;
+    if (pol->pack6 != 0 && pol->pack6 != 1) return PGQ_ERR_PARAM;
     int64_t off = 0;
     uint64_t nt = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -681,8 +687,9 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
             p.per_tensor = pol->per_tensor ? 1 : 0;
             if (p.per_tensor && p.has_awq) return PGQ_ERR_PARAM;
             if (p.per_tensor && numel >= (int64_t(1) << 32)) return PGQ_ERR_SHAPE;
+            p.packed = (pol->pack6 && p.kind == 6) ? 1 : 0;
             p.codes_off = off;
-            off = align_up(off + numel, 256);
+            off = align_up(off + (p.packed ? x.rows * (3 * ((x.cols + 3) / 4)) : numel), 256);
             p.scales_off = off;
             off = align_up(off + (p.per_tensor ? 1 : x.rows) * 2, 256);
             if (p.has_awq) {
@@ -749,6 +756,22 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
         set_grouping(descs[i], MODE_SQWA);
     }
     return run_grouped(MODE_SQWA, descs, workspace, workspace_bytes, flags, dev_status, k, 0, stream);
+}
+
+pgq_status pgq_dequant_codes(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,
+                             int32_t per_tensor, const uint16_t* awq_mult, float* out, uint32_t* dev_status,
+                             void* stream)
+{
+    (void)dev_status;
+    if (rows < 0 || cols < 0 || rows >= (int64_t(1) << 40) || cols > (int64_t(1) << 29) - 64) return PGQ_ERR_SHAPE;
+    if ((packed != 0 && packed != 1) || (per_tensor != 0 && per_tensor != 1)) return PGQ_ERR_PARAM;
+    if (rows == 0 || cols == 0) return PGQ_OK;
+    if (!codes || !scales || !out) return PGQ_ERR_NULL;
+    if (!aligned(scales, 2) || (awq_mult && !aligned(awq_mult, 2)) || !aligned(out, 4)) return PGQ_ERR_ALIGN;
+    if (const int e = launch_decode(codes, packed, rows, cols, scales, per_tensor, awq_mult, out, stream))
+        return hip_failed((hipError_t)e);
+    if (const hipError_t e = hipGetLastError()) return hip_failed(e);
+    return PGQ_OK;
 }
 
 pgq_status pgq_average_workspace(const pgq_tensor_in* t, int32_t n, size_t* workspace_bytes)

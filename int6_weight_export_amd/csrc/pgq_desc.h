@@ -16,14 +16,19 @@ constexpr uint64_t kTableMagic = 0x5047515441424c31ull;   // "PGQTABL1"
 
 enum Mode : int32_t {
     MODE_EXPORT = 0, MODE_SQWA = 1, MODE_FQ = 2, MODE_FQ_BWD = 3, MODE_EMA = 4, MODE_SWA = 5,
-    MODE_TSEL = 6     // one pass of the whole-tensor clip select (per-tensor scales)
+    MODE_TSEL = 6,    // one pass of the whole-tensor clip select (per-tensor scales)
+    MODE_EXPORT6 = 7  // export whose int6 codes are stored 4 per 3 bytes (a separate build of the
+                      // export kernels, so the plain export keeps its register budget)
 };
-constexpr int kModes = 7;
+constexpr int kModes = 8;
+template <int M>
+constexpr bool is_export = M == MODE_EXPORT || M == MODE_EXPORT6;
 enum : int32_t { IN_F32 = 0, IN_BF16 = 1 };
 enum : int32_t { KIND_F16 = 16 };
 enum : uint32_t {
     DF_VEC = 1u,          // 16-byte vector path allowed for this tensor
-    DF_TENSOR = 2u        // one scale for the whole tensor, clip from its TState
+    DF_TENSOR = 2u,       // one scale for the whole tensor, clip from its TState
+    DF_PACK6 = 4u         // codes stored 4 per 3 bytes (6-bit fields), 3 * ceil(cols / 4) per row
 };
 
 // Features a launch needs; each kernel instantiation covers a fixed set of them, and the
@@ -114,6 +119,9 @@ int max_resident_blocks(int mode, uint32_t need, bool table, int* per_cu, int* n
 // may be null); take_timing_events() hands back and clears a pending pair.
 void set_timing_events(void* start, void* stop);
 void take_timing_events(void** start, void** stop);
+// Decode of stored codes to fp32 (rows > 0, cols > 0).
+int launch_decode(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,
+                  int32_t per_tensor, const uint16_t* awq, float* out, void* stream);
 // The final pick of the whole-tensor selects: one workgroup per descriptor.
 int launch_tensor_pick(const KArgs& ka, uint32_t n_desc, void* stream);
 

@@ -161,6 +161,37 @@ __device__ __forceinline__ void store_codes(GLB int8_t* base, uint32_t e, const 
     }
 }
 
+// 6-bit code storage: four codes per three bytes, code 4g + t in bits 6t .. 6t+5 of the
+// little-endian 24-bit group g (the export's int6 artifact layout).  Lane l holds the codes of
+// chunk cu + l (cu uniform); VEC = 1 lanes pass their code to the first lane of their quad.
+template <int VEC>
+__device__ __forceinline__ void store_codes6(GLB uint8_t* row, uint32_t cu, int lane, const float (&r)[VEC],
+                                             bool valid)
+{
+    auto field = [](float q) { return (uint32_t)(int)q & 0x3Fu; };
+    auto put3 = [](GLB uint8_t* p, uint32_t w) {
+        stnt(p, (uint8_t)(w & 0xFFu));
+        stnt(p + 1, (uint8_t)((w >> 8) & 0xFFu));
+        stnt(p + 2, (uint8_t)((w >> 16) & 0xFFu));
+    };
+    if constexpr (VEC == 1) {
+        // every lane takes part (codes of lanes past the row are 0, the padding code)
+        const uint32_t f = field(r[0]);
+        const uint32_t f1 = (uint32_t)__shfl((int)f, lane + 1, 64);
+        const uint32_t f2 = (uint32_t)__shfl((int)f, lane + 2, 64);
+        const uint32_t f3 = (uint32_t)__shfl((int)f, lane + 3, 64);
+        if (valid && (lane & 3) == 0) put3(row + 3u * ((cu + (uint32_t)lane) >> 2), f | (f1 << 6) | (f2 << 12) | (f3 << 18));
+    } else {
+        if (!valid) return;
+#pragma unroll
+        for (int g = 0; g < VEC / 4; ++g) {
+            const uint32_t w = field(r[4 * g]) | (field(r[4 * g + 1]) << 6) | (field(r[4 * g + 2]) << 12) |
+                               (field(r[4 * g + 3]) << 18);
+            put3(row + 3u * ((cu + (uint32_t)lane) * (VEC / 4) + g), w);
+        }
+    }
+}
+
 template <int VEC>
 __device__ __forceinline__ void store_f32(GLB float* base, uint32_t e, const float (&v)[VEC])
 {
@@ -404,6 +435,7 @@ __device__ __forceinline__ void quant_chunk(const float (&x)[VEC], const RowCtx&
 // Uniform per-row output pointers (global address space).
 struct RowOut {
     GLB int8_t* codes;
+    GLB uint8_t* packed;      // 6-bit code storage instead of codes
     GLB void* dq;
     GLB float* mean;
     GLB uint8_t* mask;
@@ -416,7 +448,9 @@ __device__ __forceinline__ RowOut row_out(const Desc& d, int64_t row)
 {
     const int64_t o = row * d.cols;
     RowOut ro;
-    ro.codes = d.codes ? gp(d.codes) + o : nullptr;
+    const bool pack6 = (d.flags & DF_PACK6) != 0;
+    ro.codes = d.codes && !pack6 ? gp(d.codes) + o : nullptr;
+    ro.packed = d.codes && pack6 ? (GLB uint8_t*)gp(d.codes) + row * (3 * ((d.cols + 3) >> 2)) : nullptr;
     ro.dq_f32 = d.dq_dtype == IN_F32;
     ro.dq = d.dq ? (ro.dq_f32 ? (GLB void*)(gp(static_cast<float*>(d.dq)) + o)
                               : (GLB void*)(gp(static_cast<uint16_t*>(d.dq)) + o))
@@ -475,7 +509,10 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
             }
         }
     }
-    if constexpr (MODE == MODE_EXPORT) {
+    if constexpr (is_export<MODE>) {
+        if constexpr (MODE == MODE_EXPORT6) {
+            if (ro.packed) store_codes6<VEC>(ro.packed, cu, lane, r, valid);
+        }
         if (!valid) return;
         if (ro.codes) store_codes<VEC>(ro.codes + eu, e, r);
         if (ro.dq) {
@@ -911,7 +948,7 @@ __device__ __forceinline__ void row_passthrough(const Desc& d, int64_t row, int 
             if (!(fabsf(x[v]) <= 3.402823466e38f)) st |= PGQ_DEV_NONFINITE;
             else if ((h[v] & 0x7FFFu) == 0x7C00u) st |= PGQ_DEV_F16_OVF;
         }
-        if constexpr (MODE == MODE_EXPORT) {
+        if constexpr (is_export<MODE>) {
             if (hrow) store_u16<VEC>(hrow, e, h);
             if (dqrow) store_f32<VEC>(dqrow, e, y);
         } else {
@@ -1246,13 +1283,13 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
     Desc d = *p;
     asm volatile("" ::"s"(d.rows), "s"(d.cols), "s"(d.ld), "s"(d.kind), "s"(d.flags), "s"(d.rgroup),
                  "s"(d.tile_rows), "s"(d.nch), "s"(d.w), "s"(d.Q));
-    if constexpr (MODE == MODE_EXPORT) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.dq_dtype));
+    if constexpr (is_export<MODE>) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.dq_dtype));
     if constexpr (MODE == MODE_SQWA || MODE == MODE_EMA || MODE == MODE_SWA) asm volatile("" ::"s"(d.mean));
     if constexpr (MODE == MODE_TSEL) asm volatile("" ::"s"(d.tstate), "s"(d.rank_top), "s"(d.in_dtype));
-    if constexpr (MODE == MODE_EXPORT) asm volatile("" ::"s"(d.tstate));
+    if constexpr (is_export<MODE>) asm volatile("" ::"s"(d.tstate));
     if constexpr (MODE == MODE_FQ || MODE == MODE_FQ_BWD)
         asm volatile("" ::"s"(d.dq), "s"(d.scales), "s"(d.mask), "s"(d.grad), "s"(d.grad_out));
-    if constexpr ((F & F_PASS) != 0 && MODE == MODE_EXPORT) asm volatile("" ::"s"(d.f16_out));
+    if constexpr ((F & F_PASS) != 0 && is_export<MODE>) asm volatile("" ::"s"(d.f16_out));
     if constexpr ((F & F_SEL) != 0) asm volatile("" ::"s"(d.rank_top));
     if constexpr ((F & F_AWQ) != 0) asm volatile("" ::"s"(d.awq_s), "s"(d.awq_out));
     return d;
@@ -1335,6 +1372,50 @@ __global__ void __launch_bounds__(kBlock) pgq_tensor_pick_kernel(const TableHead
     for (int p = 0; p < 4; ++p) S->hist[p][tid] = 0;
 }
 
+// Decode of stored codes (the artifact loader): x = code * s, divided by a_j for AWQ tensors --
+// the export's own dequant, so the result matches it bit for bit.  Codes are int8, or 6-bit
+// fields four per three bytes (store_codes6).  One wavefront per row; lane l takes groups of
+// four columns l, l + 64, ...
+__global__ void __launch_bounds__(kBlock) pgq_decode_kernel(const uint8_t* __restrict__ codes, int32_t packed,
+                                                           int64_t rows, int64_t cols,
+                                                           const uint16_t* __restrict__ scales, int32_t per_tensor,
+                                                           const uint16_t* __restrict__ awq, float* __restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t nw = (int64_t)gridDim.x * kWaves;
+    const int64_t ngroups = (cols + 3) >> 2;
+    const int64_t rb = packed ? 3 * ngroups : cols;
+    for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < rows; row += nw) {
+        const float s = h2f(gp(scales)[per_tensor ? 0 : row]);
+        const GLB uint8_t* crow = gp(codes) + row * rb;
+        GLB float* orow = gp(out) + row * cols;
+        for (int64_t g = lane; g < ngroups; g += 64) {
+            int32_t q[4];
+            if (packed) {
+                const uint32_t w = (uint32_t)crow[3 * g] | ((uint32_t)crow[3 * g + 1] << 8) |
+                                   ((uint32_t)crow[3 * g + 2] << 16);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int32_t f = (int32_t)((w >> (6 * t)) & 0x3Fu);
+                    q[t] = f >= 32 ? f - 64 : f;
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) q[t] = 4 * g + t < cols ? (int32_t)(int8_t)crow[4 * g + t] : 0;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int64_t j = 4 * g + t;
+                if (j < cols) {
+                    float d = (float)q[t] * s;
+                    if (awq) d = d / h2f(gp(awq)[j]);       // correctly rounded divide
+                    stnt(orow + j, d);
+                }
+            }
+        }
+    }
+}
+
 // Single-matrix launches: the descriptor is a kernel argument.
 template <int MODE, uint32_t F>
 __global__ void __launch_bounds__(kBlock) pgq_single_kernel(const Desc d, KArgs ka)
@@ -1394,6 +1475,7 @@ const void* pick(int mode, uint32_t need, bool table)
     const uint32_t v = variant_of(mode, need);
     switch (mode) {
     case MODE_EXPORT: return export_like<MODE_EXPORT>(v, table);
+    case MODE_EXPORT6: return export_like<MODE_EXPORT6>(v, table);
     case MODE_SQWA: return export_like<MODE_SQWA>(v, table);
     case MODE_FQ:
         if (v == F_BF16) return kernel_ptr<MODE_FQ, F_BF16>(table);
@@ -1411,7 +1493,7 @@ const void* pick(int mode, uint32_t need, bool table)
 
 uint32_t variant_of(int mode, uint32_t need)
 {
-    if (mode == MODE_EXPORT || mode == MODE_SQWA) {
+    if (mode == MODE_EXPORT || mode == MODE_EXPORT6 || mode == MODE_SQWA) {
         for (uint32_t v : kExportVariants)
             if ((need & ~v) == 0) return v;
     } else if (mode == MODE_FQ) {
@@ -1448,6 +1530,17 @@ int launch_tensor_pick(const KArgs& ka, uint32_t n_desc, void* stream)
     const Desc* table = ka.table;
     void* args[] = {&hdr, &table, &copy};
     return (int)launch_args(reinterpret_cast<const void*>(&pgq_tensor_pick_kernel), n_desc, args,
+                            static_cast<hipStream_t>(stream));
+}
+
+int launch_decode(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,
+                  int32_t per_tensor, const uint16_t* awq, float* out, void* stream)
+{
+    const uint64_t wg = (uint64_t)((rows + kWaves - 1) / kWaves);
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(wg, 1u << 16);
+    const uint8_t* c = static_cast<const uint8_t*>(codes);
+    void* args[] = {&c, &packed, &rows, &cols, &scales, &per_tensor, &awq, &out};
+    return (int)launch_args(reinterpret_cast<const void*>(&pgq_decode_kernel), grid, args,
                             static_cast<hipStream_t>(stream));
 }
 

@@ -158,12 +158,13 @@ def _tensor_in_array(tensors: Sequence[ExportTensor]):
 
 
 def make_policy(int8_patterns=DEFAULT_INT8_PATTERNS, passthrough_below: int = 65536,
-                q_default=(6, 9999, 10000), q_sensitive=(8, 1, 1), per_tensor: bool = False):
+                q_default=(6, 9999, 10000), q_sensitive=(8, 1, 1), per_tensor: bool = False,
+                pack6: bool = False):
     pats = [p.encode() for p in int8_patterns]
     parr = (ctypes.c_char_p * max(1, len(pats)))(*pats)
     pol = pgq.pgq_policy(ctypes.cast(parr, ctypes.POINTER(ctypes.c_char_p)), len(pats), 1 if per_tensor else 0,
                          passthrough_below,
-                         pgq.pgq_qparams(*q_default), pgq.pgq_qparams(*q_sensitive))
+                         pgq.pgq_qparams(*q_default), pgq.pgq_qparams(*q_sensitive), 1 if pack6 else 0, 0)
     pol._keep = (pats, parr)
     return pol
 
@@ -213,7 +214,11 @@ class Exporter:
             if p.kind == pgq.PGQ_KIND_F16:
                 rec["f16"] = self.arena[p.f16_off:p.f16_off + 2 * rows * cols].view(torch.int16).view(t.w.shape)
             else:
-                rec["codes"] = self.arena[p.codes_off:p.codes_off + rows * cols].view(torch.int8).view(rows, cols)
+                if p.packed:
+                    rb = 3 * ((cols + 3) // 4)
+                    rec["packed"] = self.arena[p.codes_off:p.codes_off + rows * rb].view(rows, rb)
+                else:
+                    rec["codes"] = self.arena[p.codes_off:p.codes_off + rows * cols].view(torch.int8).view(rows, cols)
                 ns = 1 if p.per_tensor else rows
                 rec["scales"] = self.arena[p.scales_off:p.scales_off + 2 * ns].view(torch.int16)
                 if p.has_awq:
@@ -318,3 +323,18 @@ class Swa(_Averager):
         rc = pgq.pgq_swa_accumulate(arr, self.n, self.avg_ptrs, k, _p(ws), ws.numel(), flags, _p(self.status),
                                     _stream())
         pgq.check(rc, "pgq_swa_accumulate")
+
+
+def dequant_codes(codes: torch.Tensor, scales: torch.Tensor, cols: int, packed: bool = False,
+                  per_tensor: bool = False, awq: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 weights from stored codes (int8 [rows, cols], or packed uint8 [rows, 3 ceil(cols/4)])
+    and fp16 scales (int16 bit patterns); awq: cols fp16 multipliers (int16 bit patterns)."""
+    rows = codes.shape[0]
+    assert codes.is_contiguous() and scales.is_contiguous()
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.float32, device=codes.device)
+    rc = pgq.pgq_dequant_codes(_p(codes), 1 if packed else 0, rows, cols, _p(scales), 1 if per_tensor else 0,
+                               _p(awq), _p(out), None, _stream())
+    pgq.check(rc, "pgq_dequant_codes")
+    return out

@@ -65,13 +65,15 @@ class pgq_tensor_in(ctypes.Structure):
 class pgq_policy(ctypes.Structure):
     _fields_ = [("int8_patterns", ctypes.POINTER(ctypes.c_char_p)), ("n_patterns", ctypes.c_int32),
                 ("per_tensor", ctypes.c_int32), ("passthrough_below", ctypes.c_int64),
-                ("q_default", pgq_qparams), ("q_sensitive", pgq_qparams)]
+                ("q_default", pgq_qparams), ("q_sensitive", pgq_qparams), ("pack6", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class pgq_tensor_plan(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("has_awq", ctypes.c_int32), ("qp", pgq_qparams),
                 ("per_tensor", ctypes.c_int32), ("codes_off", ctypes.c_int64), ("scales_off", ctypes.c_int64),
-                ("f16_off", ctypes.c_int64), ("awq_off", ctypes.c_int64)]
+                ("f16_off", ctypes.c_int64), ("awq_off", ctypes.c_int64), ("packed", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -91,6 +93,7 @@ SIGNATURES = {
                                 ctypes.POINTER(_P), _P, _SZ, _U32, _P, _P]),
     "pgq_sqwa_accumulate": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan),
                                    ctypes.POINTER(_P), _I32, _P, _SZ, _U32, _P, _P]),
+    "pgq_dequant_codes": (_I32, [_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
     "pgq_average_workspace": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(_SZ)]),
     "pgq_ema_update": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(_P), ctypes.c_float, _I32, _P,
                               _SZ, _U32, _P, _P]),
@@ -152,6 +155,10 @@ def pgq_export_model(t, n, plan, arena, dq_out, workspace, workspace_bytes, flag
 def pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status, stream):
     return _lib.pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status,
                                     stream)
+
+
+def pgq_dequant_codes(codes, packed, rows, cols, scales, per_tensor, awq_mult, out, dev_status, stream):
+    return _lib.pgq_dequant_codes(codes, packed, rows, cols, scales, per_tensor, awq_mult, out, dev_status, stream)
 
 
 def pgq_average_workspace(w, n, workspace_bytes):

@@ -263,3 +263,31 @@ def test_per_tensor_plan():
     means = (ctypes.c_void_p * 8)(*([FAKE] * 8))
     assert pgq.pgq_sqwa_accumulate(arr, 8, plan, means, 1, FAKE, wb.value, 0, None,
                                    None) == pgq.PGQ_ERR_PARAM
+
+
+def test_pack6_plan_and_decode_argument_errors():
+    ts = synth.config2()[:8]
+    arr, keep = _tensor_array(ts)
+    pol, k2 = _policy()
+    pol.pack6 = 1
+    plan = (pgq.pgq_tensor_plan * 8)()
+    ab, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert pgq.pgq_export_plan(arr, 8, ctypes.byref(pol), plan, ctypes.byref(ab), ctypes.byref(wb)) == 0
+    for i, t in enumerate(ts):
+        if plan[i].kind == 6:
+            rows, cols = oracle.as_rows(t.shape)
+            assert plan[i].packed == 1
+            assert plan[i].scales_off - plan[i].codes_off == -(-rows * 3 * ((cols + 3) // 4) // 256) * 256
+        else:
+            assert plan[i].packed == 0                 # int8 and fp16 tensors are not packed
+    pol.pack6 = 3
+    assert pgq.pgq_export_plan(arr, 8, ctypes.byref(pol), plan, ctypes.byref(ab),
+                               ctypes.byref(wb)) == pgq.PGQ_ERR_PARAM
+    dq = pgq.pgq_dequant_codes
+    assert dq(FAKE, 1, 0, 512, FAKE, 0, None, FAKE, None, None) == pgq.PGQ_OK           # empty
+    assert dq(FAKE, 1, -1, 512, FAKE, 0, None, FAKE, None, None) == pgq.PGQ_ERR_SHAPE
+    assert dq(FAKE, 2, 4, 512, FAKE, 0, None, FAKE, None, None) == pgq.PGQ_ERR_PARAM
+    assert dq(FAKE, 1, 4, 512, FAKE, 5, None, FAKE, None, None) == pgq.PGQ_ERR_PARAM
+    assert dq(None, 1, 4, 512, FAKE, 0, None, FAKE, None, None) == pgq.PGQ_ERR_NULL
+    assert dq(FAKE, 1, 4, 512, FAKE + 1, 0, None, FAKE, None, None) == pgq.PGQ_ERR_ALIGN
+    assert dq(FAKE, 1, 4, 512, FAKE, 0, None, FAKE + 2, None, None) == pgq.PGQ_ERR_ALIGN
