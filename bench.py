@@ -257,38 +257,34 @@ def workload_pack6(copies, torch, ops):
 
 
 def workload_decode(copies, torch, ops):
-    """Decode of the exported 9-layer artifact (6-bit int6 codes, int8 tok_emb, fp16 scales) back to
-    fp32 weights: one pgq_dequant_codes call per integer tensor."""
+    """Decode of the exported 9-layer artifact (6-bit int6 codes, int8 tok_emb, fp16 row scales,
+    fp16 vectors) back to fp32 weights: one grouped pgq_dequant_model launch per step."""
     tensors = synth.config2()
     sets = []
-    nbytes = rows = 0
-    for k in range(copies):
+    for _ in range(copies):
         ex = ops.Exporter([ops.ExportTensor(t.name, _dev(t.data, torch)) for t in tensors],
                           ops.make_policy(pack6=True), want_dq=False)
         ex.run()
-        jobs = []
-        for t, o in zip(tensors, ex.outputs()):
-            if o["kind"] == 16:
-                continue
-            r, c = (t.shape[0], t.numel // t.shape[0])
-            packed = "packed" in o
-            codes = o["packed"] if packed else o["codes"]
-            out = torch.empty(r, c, dtype=torch.float32, device="cuda")
-            jobs.append((codes, o["scales"], c, packed, out))
-            if k == 0:
-                nbytes += codes.numel() + 2 * r + 4 * r * c
-                rows += r
-        sets.append(jobs)
+        outs = ex.decode()
+        sets.append((ex, outs))
+    import oracle
 
-    def step(i):
-        for codes, scales, c, packed, out in sets[i % len(sets)]:
-            ops.dequant_codes(codes, scales, c, packed=packed, out=out)
-
+    pol = oracle.Policy(pack6=True)
+    nbytes = rows = 0
+    for t in tensors:
+        r, c = oracle.as_rows(t.shape)
+        kind = oracle.tensor_kind(t.name, t.numel, pol)
+        nbytes += 4 * t.numel
+        if kind == oracle.KIND_F16:
+            nbytes += 2 * t.numel
+        else:
+            nbytes += (r * 3 * ((c + 3) // 4) if kind == oracle.KIND_INT6 else t.numel) + 2 * r
+            rows += r
     cfg = {"workload": "decode of the exported 9-layer d=512 artifact (int6 codes four per three bytes, int8 "
-                       "tok_emb.weight, fp16 row scales) to fp32 weights, one call per tensor",
-           "tensors": len(sets[0]), "params": int(sum(t.numel for t in tensors if t.numel >= 65536))}
-    return Workload("decode", cfg["workload"], nbytes, rows, step, lambda: [0], cfg, "pgq_decode_kernel",
-                    launches=len(sets[0]), timed_calls=[(ops, "dequant_codes")]), None
+                       "tok_emb.weight, fp16 row scales, fp16 vectors) to fp32 weights, one launch",
+           "tensors": len(tensors), "params": int(sum(t.numel for t in tensors))}
+    return Workload("decode", cfg["workload"], nbytes, rows, lambda i: sets[i % len(sets)][0].decode(sets[i % len(sets)][1]),
+                    lambda: [int(s[0].status.item()) for s in sets], cfg, "pgq_table_kernel<8, 1u>"), None
 
 
 def workload_tensor(copies, torch, ops):
@@ -369,7 +365,7 @@ def main() -> int:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer is "
               f"row-parallel within a GPU and this build runs no collectives)", file=sys.stderr)
         return 2
-    steps = args.steps if args.steps is not None else {"sqwa": 50, "decode": 200}.get(args.mode, 1000)
+    steps = args.steps if args.steps is not None else {"sqwa": 50}.get(args.mode, 1000)
     warmup = args.warmup if args.warmup is not None else (3 if args.mode == "sqwa" else 50)
 
     import torch

@@ -234,6 +234,15 @@ pgq_status pgq_dequant_codes(const void* codes, int32_t packed, int64_t rows, in
                              int32_t per_tensor, const uint16_t* awq_mult, float* out, uint32_t* dev_status,
                              void* stream);
 
+/* The whole exported model back to fp32 in one grouped launch: for each tensor i with out[i]  */
+/* non-NULL (fp32 rows x cols dense), the decode above of its arena regions (plan[i] as        */
+/* pgq_export_plan wrote it), or fp32 of the stored fp16 values for passthrough tensors.      */
+/* t supplies the shapes only (w and name are ignored).  workspace: at least the              */
+/* workspace_bytes pgq_export_plan reported (descriptor table; PGQ_TABLE_RESIDENT as usual). */
+pgq_status pgq_dequant_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan* plan, const void* arena,
+                             float* const* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                             uint32_t* dev_status, void* stream);
+
 /* ------------------------------------------------------------------------------------------ */
 /* Weight averaging without quantization, grouped over n tensors in one launch.               */
 /* w[i]: the weights (fp32 or bf16, rows x cols, row stride ld; awq_s must be NULL; name is    */

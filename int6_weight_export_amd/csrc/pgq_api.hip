@@ -224,7 +224,8 @@ void set_grouping(Desc& d, int mode)
 {
     int R = 1;
     d.nch = 0;
-    if (mode != MODE_FQ_BWD && mode != MODE_EMA && mode != MODE_SWA && d.kind != KIND_F16 && d.cols > 0) {
+    if (mode != MODE_FQ_BWD && mode != MODE_EMA && mode != MODE_SWA && mode != MODE_DECODE && d.kind != KIND_F16 &&
+        d.cols > 0) {
         const bool vec = (d.flags & DF_VEC) != 0;
         const int64_t nchunk = vec ? d.cols / (d.in_dtype == IN_F32 ? 4 : 8) : d.cols;
         const int ncht = vec ? (d.in_dtype == IN_F32 ? 8 : 4) : 16;
@@ -302,9 +303,12 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
     std::vector<uint32_t> start2(n + 1, 0);
     uint64_t total2 = 0;
     int passes = 0;
+    // (only an export selects; a decode's DF_TENSOR just means "scale 0 for every row")
+    const bool selects = mode == MODE_EXPORT || mode == MODE_EXPORT6;
     for (size_t i = 0; i < n; ++i) {
         start2[i] = (uint32_t)total2;
-        if (descs[i].flags & DF_TENSOR) {
+        if (selects && (descs[i].flags & DF_TENSOR)) {
+            if (!descs[i].w && tiles_for(descs[i]) > 0) return PGQ_ERR_NULL;   // the select reads the weights
             total2 += (tiles_for(descs[i]) + kSelGroup - 1) / kSelGroup;
             passes = std::max(passes, descs[i].rank_top > 1 ? 4 : 1);
             descs[i].tstate = reinterpret_cast<TState*>(static_cast<uint8_t*>(ws) + L.state_off) + i;
@@ -772,6 +776,51 @@ pgq_status pgq_dequant_codes(const void* codes, int32_t packed, int64_t rows, in
         return hip_failed((hipError_t)e);
     if (const hipError_t e = hipGetLastError()) return hip_failed(e);
     return PGQ_OK;
+}
+
+pgq_status pgq_dequant_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan* plan, const void* arena,
+                             float* const* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                             uint32_t* dev_status, void* stream)
+{
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (n == 0) return PGQ_OK;
+    if (!t || !plan || !arena || !out) return PGQ_ERR_NULL;
+    if (!aligned(arena, 256)) return PGQ_ERR_ALIGN;
+    const uint8_t* a = static_cast<const uint8_t*>(arena);
+    std::vector<Desc> descs;
+    descs.reserve((size_t)n);
+    for (int32_t i = 0; i < n; ++i) {
+        if (!shape_ok(t[i].rows, t[i].cols, t[i].ld)) return PGQ_ERR_SHAPE;
+        const pgq_tensor_plan& p = plan[i];
+        const pgq_status st = check_plan_entry(p);
+        if (st != PGQ_OK) return st;
+        if (!out[i] || t[i].rows == 0 || t[i].cols == 0) continue;
+        if (!aligned(out[i], 4)) return PGQ_ERR_ALIGN;
+        Desc d = blank_desc();
+        d.rows = t[i].rows;
+        d.cols = t[i].cols;
+        d.ld = t[i].cols;
+        d.dq = out[i];
+        if (p.kind == PGQ_KIND_F16) {
+            if (p.f16_off < 0) return PGQ_ERR_PARAM;
+            d.kind = KIND_F16;
+            d.f16_out = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(a + p.f16_off));
+        } else {
+            if (p.codes_off < 0 || p.scales_off < 0 || (p.has_awq && p.awq_off < 0)) return PGQ_ERR_PARAM;
+            d.kind = p.kind;
+            d.codes = reinterpret_cast<int8_t*>(const_cast<uint8_t*>(a + p.codes_off));
+            d.scales = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(a + p.scales_off));
+            if (p.has_awq) d.awq_out = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(a + p.awq_off));
+            if (p.packed) d.flags |= DF_PACK6;
+            if (p.per_tensor) d.flags |= DF_TENSOR;
+        }
+        // vector path: whole groups of four, 16-byte fp32 stores, 4-byte int8 code loads
+        if (d.cols % 4 == 0 && aligned(out[i], 16)) d.flags |= DF_VEC;
+        set_grouping(d, MODE_DECODE);
+        descs.push_back(d);
+    }
+    if (descs.empty()) return PGQ_OK;
+    return run_grouped(MODE_DECODE, descs, workspace, workspace_bytes, flags, dev_status, 0, 0, stream);
 }
 
 pgq_status pgq_average_workspace(const pgq_tensor_in* t, int32_t n, size_t* workspace_bytes)

@@ -17,10 +17,11 @@ constexpr uint64_t kTableMagic = 0x5047515441424c31ull;   // "PGQTABL1"
 enum Mode : int32_t {
     MODE_EXPORT = 0, MODE_SQWA = 1, MODE_FQ = 2, MODE_FQ_BWD = 3, MODE_EMA = 4, MODE_SWA = 5,
     MODE_TSEL = 6,    // one pass of the whole-tensor clip select (per-tensor scales)
-    MODE_EXPORT6 = 7  // export whose int6 codes are stored 4 per 3 bytes (a separate build of the
+    MODE_EXPORT6 = 7, // export whose int6 codes are stored 4 per 3 bytes (a separate build of the
                       // export kernels, so the plain export keeps its register budget)
+    MODE_DECODE = 8   // stored artifact (codes / packed codes / fp16) back to fp32
 };
-constexpr int kModes = 8;
+constexpr int kModes = 9;
 template <int M>
 constexpr bool is_export = M == MODE_EXPORT || M == MODE_EXPORT6;
 enum : int32_t { IN_F32 = 0, IN_BF16 = 1 };

@@ -1046,6 +1046,58 @@ __device__ __forceinline__ void row_average(const Desc& d, int64_t row, int lane
     }
 }
 
+// ---- decode of one stored row (grouped whole-model decode) ---------------------------------------
+// Integer kinds: x = code * s (/ a_j), the export's own dequant; fp16 passthrough: fp32 of the
+// stored half.  Codes are int8 or 6-bit packed (DF_PACK6); lane l takes groups of four columns.
+__device__ __forceinline__ void row_decode(const Desc& d, int64_t row, int lane)
+{
+    const int64_t cols = d.cols;
+    const int64_t ngroups = (cols + 3) >> 2;
+    GLB float* orow = gp(static_cast<float*>(d.dq)) + row * cols;
+    if (d.kind == KIND_F16) {
+        const GLB uint16_t* hrow = gp(d.f16_out) + row * cols;
+        for (int64_t j = lane; j < cols; j += 64) stnt(orow + j, h2f(hrow[j]));
+        return;
+    }
+    const bool packed = (d.flags & DF_PACK6) != 0;
+    const bool vec = (d.flags & DF_VEC) != 0;
+    const float s = h2f(gp(d.scales)[(d.flags & DF_TENSOR) ? 0 : row]);
+    const GLB uint8_t* crow = (const GLB uint8_t*)gp(d.codes) + row * (packed ? 3 * ngroups : cols);
+    const GLB uint16_t* awq = d.awq_out ? gp(d.awq_out) : nullptr;
+    for (int64_t g = lane; g < ngroups; g += 64) {
+        int32_t q[4];
+        if (packed) {
+            const uint32_t w = (uint32_t)crow[3 * g] | ((uint32_t)crow[3 * g + 1] << 8) | ((uint32_t)crow[3 * g + 2] << 16);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int32_t f = (int32_t)((w >> (6 * t)) & 0x3Fu);
+                q[t] = f >= 32 ? f - 64 : f;
+            }
+        } else if (vec) {                                   // four int8 codes, 4-byte aligned
+            const uint32_t w = *at<uint32_t>(crow, (uint32_t)(4 * g));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) q[t] = (int32_t)(int8_t)((w >> (8 * t)) & 0xFFu);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) q[t] = 4 * g + t < cols ? (int32_t)(int8_t)crow[4 * g + t] : 0;
+        }
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t j = 4 * g + t;
+            v[t] = (float)q[t] * s;
+            if (awq && j < cols) v[t] = v[t] / h2f(awq[j]);    // correctly rounded divide
+        }
+        if (vec) {                                          // cols % 4 == 0, 16-byte aligned rows
+            stnt(at<f32x4>(orow, (uint32_t)(16 * g)), f32x4{v[0], v[1], v[2], v[3]});
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (4 * g + t < cols) stnt(orow + 4 * g + t, v[t]);
+        }
+    }
+}
+
 template <int MODE, uint32_t F>
 __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nrows, int lane, uint32_t* hist,
                                               const float* awq_lds, const KArgs& ka, uint32_t& st)
@@ -1055,7 +1107,9 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nr
     constexpr bool LONG = (F & F_LONG) != 0;
     constexpr bool SCALAR = (F & F_SCALAR) != 0;
     const bool vec = (d.flags & DF_VEC) != 0;
-    if constexpr (MODE == MODE_EMA || MODE == MODE_SWA) {
+    if constexpr (MODE == MODE_DECODE) {
+        for (int r = 0; r < nrows; ++r) row_decode(d, row + r, lane);
+    } else if constexpr (MODE == MODE_EMA || MODE == MODE_SWA) {
         for (int r = 0; r < nrows; ++r) {
             if constexpr ((F & F_F32) != 0) {
                 if (d.in_dtype == IN_F32) {
@@ -1286,6 +1340,7 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
     if constexpr (is_export<MODE>) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.dq_dtype));
     if constexpr (MODE == MODE_SQWA || MODE == MODE_EMA || MODE == MODE_SWA) asm volatile("" ::"s"(d.mean));
     if constexpr (MODE == MODE_TSEL) asm volatile("" ::"s"(d.tstate), "s"(d.rank_top), "s"(d.in_dtype));
+    if constexpr (MODE == MODE_DECODE) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.f16_out), "s"(d.awq_out));
     if constexpr (is_export<MODE>) asm volatile("" ::"s"(d.tstate));
     if constexpr (MODE == MODE_FQ || MODE == MODE_FQ_BWD)
         asm volatile("" ::"s"(d.dq), "s"(d.scales), "s"(d.mask), "s"(d.grad), "s"(d.grad_out));
@@ -1485,6 +1540,7 @@ const void* pick(int mode, uint32_t need, bool table)
     case MODE_EMA: return average_kernel<MODE_EMA>(v, table);
     case MODE_TSEL: return average_kernel<MODE_TSEL>(v, table);
     case MODE_SWA: return average_kernel<MODE_SWA>(v, table);
+    case MODE_DECODE: return table ? reinterpret_cast<const void*>(&pgq_table_kernel<MODE_DECODE, F_F32>) : nullptr;
     default: return nullptr;
     }
 }

@@ -200,6 +200,26 @@ class Exporter:
         pgq.check(rc, "pgq_export_model")
         self._uploaded = True
 
+    def decode(self, out: Optional[List[torch.Tensor]] = None, reuse_table: bool = True) -> List[torch.Tensor]:
+        """fp32 weights from the arena (the stored artifact), every tensor in one launch."""
+        dev = self.arena.device
+        if out is None:
+            out = [torch.empty(t.w.shape, dtype=torch.float32, device=dev) for t in self.tensors]
+        key = tuple(o.data_ptr() for o in out)
+        cached = getattr(self, "_decode_table", None)
+        flags = 0
+        if cached is not None and cached[0] == key and reuse_table:
+            ptrs, ws = cached[1], cached[2]
+            flags = pgq.PGQ_TABLE_RESIDENT
+        else:
+            ptrs = (ctypes.c_void_p * self.n)(*[o.data_ptr() for o in out])
+            ws = torch.empty(self.workspace.numel(), dtype=torch.uint8, device=dev)
+            self._decode_table = (key, ptrs, ws)
+        rc = pgq.pgq_dequant_model(self.arr, self.n, self.plan, _p(self.arena), ptrs, _p(ws), ws.numel(), flags,
+                                   _p(self.status), _stream())
+        pgq.check(rc, "pgq_dequant_model")
+        return out
+
     def kinds(self) -> List[int]:
         return [self.plan[i].kind for i in range(self.n)]
 

@@ -291,3 +291,23 @@ def test_pack6_plan_and_decode_argument_errors():
     assert dq(None, 1, 4, 512, FAKE, 0, None, FAKE, None, None) == pgq.PGQ_ERR_NULL
     assert dq(FAKE, 1, 4, 512, FAKE + 1, 0, None, FAKE, None, None) == pgq.PGQ_ERR_ALIGN
     assert dq(FAKE, 1, 4, 512, FAKE, 0, None, FAKE + 2, None, None) == pgq.PGQ_ERR_ALIGN
+
+
+def test_dequant_model_argument_errors():
+    ts = synth.config2()[:4]
+    arr, keep = _tensor_array(ts)
+    pol, k2 = _policy()
+    plan = (pgq.pgq_tensor_plan * 4)()
+    ab, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert pgq.pgq_export_plan(arr, 4, ctypes.byref(pol), plan, ctypes.byref(ab), ctypes.byref(wb)) == 0
+    outs = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    dm = pgq.pgq_dequant_model
+    assert dm(arr, 0, plan, None, None, None, 0, 0, None, None) == pgq.PGQ_OK
+    assert dm(arr, 4, plan, None, outs, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_NULL
+    assert dm(arr, 4, plan, FAKE + 64, outs, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_ALIGN
+    assert dm(arr, 4, plan, FAKE, outs, FAKE, 64, 0, None, None) == pgq.PGQ_ERR_WORKSPACE
+    outs[1] = FAKE + 2
+    assert dm(arr, 4, plan, FAKE, outs, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_ALIGN
+    outs[1] = FAKE
+    plan[0].kind = 9
+    assert dm(arr, 4, plan, FAKE, outs, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM

@@ -114,3 +114,38 @@ def test_awq_and_per_tensor_packed():
     named2 = [(t.name, t.data) for t in synth.stress_s1()[:8]]
     ex2 = _export(named2, {"q_default": (6, 99, 100), "per_tensor": True})
     _check(ex2, named2, oracle.Policy(q6=(6, 99, 100), pack6=True, per_tensor=True))
+
+
+@pytest.mark.parametrize("pol_kwargs,opol_kwargs", [
+    ({}, {}),
+    ({"pack6": True}, {"pack6": True}),
+    ({"pack6": True, "per_tensor": True, "q_default": (6, 99, 100)},
+     {"pack6": True, "per_tensor": True, "q6": (6, 99, 100)}),
+])
+def test_whole_model_decode(pol_kwargs, opol_kwargs):
+    say(f"whole-model decode {pol_kwargs}")
+    named = [(t.name, t.data) for t in synth.config2()]
+    ex = ops.Exporter([ops.ExportTensor(nm, dev(w)) for nm, w in named], ops.make_policy(**pol_kwargs),
+                      want_dq=False)
+    ex.run()
+    ref = oracle.export(named, oracle.Policy(**opol_kwargs))
+    for rep in range(2):                               # second call on the resident table
+        outs = ex.decode()
+        torch.cuda.synchronize()
+        for o, r, (nm, _) in zip(outs, ref, named):
+            f32_bits_equal(f32(o).reshape(-1), r["dq"].reshape(-1), f"{nm} decode {rep}")
+
+
+def test_whole_model_decode_awq():
+    say("whole-model decode of an AWQ export")
+    ts = synth.config4()[:10]
+    awq = {t.name: t.awq_s for t in ts if t.awq_s is not None}
+    named = [(t.name, t.data) for t in ts]
+    ex = ops.Exporter([ops.ExportTensor(nm, dev(w), None if nm not in awq else dev(awq[nm])) for nm, w in named],
+                      ops.make_policy(q_default=(6, 1, 1), pack6=True), want_dq=False)
+    ex.run()
+    outs = ex.decode()
+    torch.cuda.synchronize()
+    ref = oracle.export(named, oracle.Policy(q6=(6, 1, 1), pack6=True), awq=awq)
+    for o, r, (nm, _) in zip(outs, ref, named):
+        f32_bits_equal(f32(o).reshape(-1), r["dq"].reshape(-1), f"{nm} decode")
