@@ -10,7 +10,7 @@ from .lib import (  # noqa: F401
     ORC_NONFINITE, ORC_SCALE_OVF, ORC_F16_OVF, ORC_BAD_AWQ,
     load, build, f32_to_f16, f16_to_f32, f32_to_bf16, bf16_to_f32, percentile_rank,
     quantize_rows, quantize_tensor, awq_multipliers, fakequant_rows, f16_passthrough, sqwa_update, ema_update, swa_update,
-    pack6_row_bytes, pack6, unpack6, dequant,
+    pack6_row_bytes, pack6, unpack6, dequant, qgemm_bf16,
 )
 from .policy import (  # noqa: F401
     Policy, DEFAULT_INT8_PATTERNS, KIND_F16, KIND_INT6, KIND_INT8,

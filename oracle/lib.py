@@ -65,6 +65,8 @@ def load():
             lib.orc_unpack6_rows.restype = None
             lib.orc_dequant_rows.argtypes = [_P, _I64, _I64, _P, _I32, _P, _P]
             lib.orc_dequant_rows.restype = None
+            lib.orc_qgemm_bf16.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P]
+            lib.orc_qgemm_bf16.restype = None
             lib.orc_awq_multipliers.argtypes = [_P, _I64, _P]
             lib.orc_awq_multipliers.restype = _U32
             lib.orc_fakequant_rows.argtypes = [_P, _I64, _I64, _I64, _I32, _U32, _U32, _P, _P, _P, _P, _P, _P]
@@ -251,3 +253,17 @@ def dequant(codes, scales, per_tensor: bool = False, awq=None) -> np.ndarray:
     out = np.empty((rows, cols), dtype=np.float32)
     load().orc_dequant_rows(_ptr(c), rows, cols, _ptr(s), 1 if per_tensor else 0, _ptr(a), _ptr(out))
     return out
+
+
+def qgemm_bf16(x_bf16, codes, scales):
+    """Y = X What^T in double, What = bf16(code * s) per row; returns (y, sum |x What|)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    c = np.ascontiguousarray(codes, dtype=np.int8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    M, K = x.shape
+    N = c.shape[0]
+    assert c.shape == (N, K) and s.shape == (N,)
+    y = np.empty((M, N), dtype=np.float64)
+    b = np.empty((M, N), dtype=np.float64)
+    load().orc_qgemm_bf16(_ptr(x), M, K, K, _ptr(c), K, _ptr(s), N, _ptr(y), _ptr(b))
+    return y, b

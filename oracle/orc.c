@@ -282,6 +282,37 @@ void orc_dequant_rows(const int8_t* codes, int64_t rows, int64_t cols, const uin
     }
 }
 
+/* The QAT forward's consumer GEMM with the fake-quantized weights (STE fake quantization in the
+ * forward pass, PR #69 card section Other): Y = X * What^T, X bf16 [M x K] (row stride ldx),
+ * What[n][k] = bf16_rne(fp32(code[n][k] * s_n)) -- the STE forward's dequantized weight -- from
+ * int8 codes [N x K] (row stride ldc) and fp16 row scales.  Accumulated in double: every product
+ * of two bf16 values is exact in double, so y is the exact sum up to double rounding.  bound[m][n]
+ * receives sum_k |x * What| (for the tolerance of a binary32 accumulation). */
+void orc_qgemm_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
+                    const uint16_t* scales, int64_t N, double* y, double* bound)
+{
+    float* wq = (float*)malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(float));
+    for (int64_t n = 0; n < N; ++n) {
+        float s = orc_f16_to_f32(scales[n]);
+        for (int64_t k = 0; k < K; ++k) {
+            float d = (float)codes[n * ldc + k] * s;
+            wq[n * K + k] = orc_bf16_to_f32(orc_f32_to_bf16(d));
+        }
+    }
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = (double)orc_bf16_to_f32(x[m * ldx + k]) * (double)wq[n * K + k];
+                acc += p;
+                mag += fabs(p);
+            }
+            y[m * N + n] = acc;
+            if (bound) bound[m * N + n] = mag;
+        }
+    free(wq);
+}
+
 /* AWQ column multipliers a_j = fp16_rne(sqrt(s_j)) (exponent 1/2), s_j > 0 and finite. */
 uint32_t orc_awq_multipliers(const float* s, int64_t cols, uint16_t* a)
 {
