@@ -34,6 +34,7 @@ import synth  # noqa: E402
 
 METRIC = "quantizer GB/s (bytes in+out) and % of MI355X HBM peak, int6 per-row"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0          # dense bf16 matrix-core peak of the MI355X
 KERNEL_SOURCES = ["int6_weight_export_amd/csrc/pgq_kernels.hip", "int6_weight_export_amd/csrc/pgq_api.hip",
                   "int6_weight_export_amd/csrc/pgq_desc.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_export_gpt9.json")
@@ -92,10 +93,12 @@ def cpu_baseline(tensors, min_seconds: float = 10.0, max_passes: int = 30) -> di
 class Workload:
     """One bench workload: `step(i)` enqueues one step on input set i % copies."""
 
-    def __init__(self, name, desc, nbytes, rows, step, statuses, config, kernel, launches=1, timed_calls=()):
+    def __init__(self, name, desc, nbytes, rows, step, statuses, config, kernel, launches=1, timed_calls=(),
+                 flops=None):
         self.name, self.desc, self.nbytes, self.rows = name, desc, nbytes, rows
         self.step, self.statuses, self.config, self.kernel = step, statuses, config, kernel
         self.launches, self.timed_calls = launches, list(timed_calls)   # library calls per step
+        self.flops = flops                       # a contraction: roofline against the MFMA peak
 
 
 def _dev(a, torch):
@@ -287,6 +290,31 @@ def workload_decode(copies, torch, ops):
                     lambda: [int(s[0].status.item()) for s in sets], cfg, "pgq_table_kernel<8, 1u>"), None
 
 
+def workload_qgemm(copies, torch, ops):
+    """The QAT forward's consumer GEMM with the STE dequantization fused in: 16384 tokens through
+    the d=528 unified Q/K/V projection (What 1584 x 528 from int8 codes + fp16 row scales),
+    bf16 MFMA with fp32 accumulation."""
+    import oracle
+
+    M, N, K = 16384, 1584, 528
+    rng = np.random.default_rng(0)
+    w = oracle.f32_to_bf16((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    fq = oracle.fakequant_rows(w, 31)
+    codes = torch.from_numpy(fq["codes"]).cuda()
+    scales = torch.from_numpy(fq["scales"].view(np.int16)).cuda()
+    sets = []
+    for k in range(copies):
+        x = torch.randn(M, K, generator=torch.Generator().manual_seed(k)).to(torch.bfloat16).cuda()
+        sets.append((x, torch.empty(M, N, dtype=torch.float32, device="cuda")))
+    nbytes = 2 * M * K + N * K + 2 * N + 4 * M * N
+    cfg = {"workload": "fused-dequant GEMM of the QAT forward: Y[16384 x 1584] = X[16384 x 528] (bf16) times "
+                       "bf16(code * s)^T from int8 codes and fp16 row scales, fp32 accumulation on MFMA",
+           "M": M, "N": N, "K": K}
+    return Workload("qgemm", cfg["workload"], nbytes, M,
+                    lambda i: ops.qgemm(sets[i % len(sets)][0], codes, scales, out=sets[i % len(sets)][1]),
+                    lambda: [0], cfg, "pgq_qgemm_kernel", flops=2 * M * N * K), None
+
+
 def workload_tensor(copies, torch, ops):
     """Per-tensor scales: the 9-layer export with one scale per integer tensor, the clip at the
     99.99th percentile of |w| over the whole tensor (int8 tok_emb: absmax).  A step is the
@@ -352,7 +380,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 1000; 50 for --mode sqwa)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 50; 3 for --mode sqwa)")
     ap.add_argument("--mode", default="export", choices=["export", "awq", "batch", "select", "fakequant", "sqwa", "ema", "swa", "tensor",
-                                                    "pack6", "decode"],
+                                                    "pack6", "decode", "qgemm"],
                     help="export (default): the 9-layer whole-model export; the others time the remaining "
                          "rows of the path")
     ap.add_argument("--copies", type=int, default=6, help="input/output sets used in rotation")
@@ -376,7 +404,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     make = {"export": workload_export, "awq": workload_awq, "batch": workload_batch, "select": workload_select,
             "ema": workload_ema, "swa": workload_swa, "tensor": workload_tensor, "pack6": workload_pack6,
-            "decode": workload_decode,
+            "decode": workload_decode, "qgemm": workload_qgemm,
             "sqwa": workload_sqwa}
     if args.mode == "fakequant":
         wl, tensors = workload_fakequant(args.copies, torch, ops, pgq)
@@ -460,17 +488,24 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.mode == "fakequant" else "f32",
+        "dtype": "bf16" if args.mode in ("fakequant", "qgemm") else "f32",
         "data": "synthetic",
         "config": config,
-        "roofline": {
+        "roofline": ({
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-        },
+        } if wl.flops is None else {
+            "bound": "mfma",
+            "achieved": round(wl.flops / k_step_s / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(wl.flops / k_step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        }),
         "kernel": wl.kernel,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernel_us_per_step": round(k_step_s * 1e6, 3),

@@ -244,6 +244,20 @@ pgq_status pgq_dequant_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor
                              uint32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------------------------ */
+/* The QAT forward's consumer GEMM with the STE dequantization fused in.  Source: "SubSixteen   */
+/* v2" card (PR #69), section Other: STE fake quantization in the forward pass -- the layer's  */
+/* matmul consumes What[n][k] = bf16(fp32(code[n][k] * s_n)), which this call forms on the fly  */
+/* from the codes and scales instead of reading a materialised bf16 weight.                    */
+/*   Y[m][n] = sum_k X[m][k] * What[n][k], accumulated in fp32 on the matrix cores (MFMA)      */
+/*   x       device bf16 bit patterns, M x K, row stride ldx >= K                              */
+/*   codes   device int8, N x K, row stride ldc >= K (e.g. the fake-quant call's codes output)  */
+/*   scales  device fp16 bit patterns, N (one per weight row)                                   */
+/*   y       device fp32, M x N, row stride ldy >= N (written, not accumulated into)           */
+/* M <= 65535 * 128.  K = 0 writes zeros.  Asynchronous on stream.                             */
+pgq_status pgq_qgemm_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
+                          const uint16_t* scales, int64_t N, float* y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
 /* Weight averaging without quantization, grouped over n tensors in one launch.               */
 /* w[i]: the weights (fp32 or bf16, rows x cols, row stride ld; awq_s must be NULL; name is    */
 /* ignored).  The averages are caller-owned fp32 device buffers, rows x cols dense, updated in */

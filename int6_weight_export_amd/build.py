@@ -16,7 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpgq.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("pgq_api.hip", "pgq_kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("pgq_api.hip", "pgq_kernels.hip", "pgq_gemm.hip")]
 HEADERS = [os.path.join(HERE, "csrc", "pgq_desc.h"), os.path.join(ROOT, "include", "pgq.h")]
 ARCH = os.environ.get("PGQ_OFFLOAD_ARCH", "gfx950")
 

@@ -762,6 +762,22 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
     return run_grouped(MODE_SQWA, descs, workspace, workspace_bytes, flags, dev_status, k, 0, stream);
 }
 
+pgq_status pgq_qgemm_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
+                          const uint16_t* scales, int64_t N, float* y, int64_t ldy, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || ldx < K || ldc < K || ldy < N) return PGQ_ERR_SHAPE;
+    if (M > (int64_t)65535 * 128 || N > ((int64_t)1 << 31) || K > ((int64_t)1 << 31)) return PGQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return PGQ_OK;
+    if (!y || (K > 0 && (!x || !codes || !scales))) return PGQ_ERR_NULL;
+    if ((x && !aligned(x, 2)) || (scales && !aligned(scales, 2)) || !aligned(y, 4)) return PGQ_ERR_ALIGN;
+    uint32_t f = 0;
+    if (x && ldx % 8 == 0 && aligned(x, 16)) f |= 1u;
+    if (codes && ldc % 16 == 0 && aligned(codes, 16)) f |= 2u;
+    if (const int e = launch_qgemm(x, M, K, ldx, codes, ldc, scales, N, y, ldy, f, stream)) return hip_failed((hipError_t)e);
+    if (const hipError_t e = hipGetLastError()) return hip_failed(e);
+    return PGQ_OK;
+}
+
 pgq_status pgq_dequant_codes(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,
                              int32_t per_tensor, const uint16_t* awq_mult, float* out, uint32_t* dev_status,
                              void* stream)

@@ -6,6 +6,7 @@
 // tile of each tensor, a prefix sum) and tile_desc[n_tiles] (the tensor of each tile).
 // Single-matrix calls pass one Desc by value in the kernel arguments.
 #pragma once
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace pgq {
@@ -120,6 +121,11 @@ int max_resident_blocks(int mode, uint32_t need, bool table, int* per_cu, int* n
 // may be null); take_timing_events() hands back and clears a pending pair.
 void set_timing_events(void* start, void* stop);
 void take_timing_events(void** start, void** stop);
+// Any kernel with a 3-D grid, taking a pending timing-event pair like the others.
+hipError_t launch_plain(const void* fn, dim3 grid, dim3 block, void** args, void* stream);
+// The fused-dequant GEMM (pgq_gemm.hip); flags: bit 0 X rows 16-byte loadable, bit 1 code rows.
+int launch_qgemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
+                 const uint16_t* scales, int64_t N, float* y, int64_t ldy, uint32_t flags, void* stream);
 // Decode of stored codes to fp32 (rows > 0, cols > 0).
 int launch_decode(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,
                   int32_t per_tensor, const uint16_t* awq, float* out, void* stream);

@@ -1589,6 +1589,17 @@ int launch_tensor_pick(const KArgs& ka, uint32_t n_desc, void* stream)
                             static_cast<hipStream_t>(stream));
 }
 
+hipError_t launch_plain(const void* fn, dim3 grid, dim3 block, void** args, void* stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (t_start || t_stop) {
+        hipEvent_t a = t_start, b = t_stop;
+        t_start = t_stop = nullptr;
+        return hipExtLaunchKernel(fn, grid, block, args, 0, s, a, b, 0);
+    }
+    return hipLaunchKernel(fn, grid, block, args, 0, s);
+}
+
 int launch_decode(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,
                   int32_t per_tensor, const uint16_t* awq, float* out, void* stream)
 {

@@ -358,3 +358,19 @@ def dequant_codes(codes: torch.Tensor, scales: torch.Tensor, cols: int, packed: 
                                _p(awq), _p(out), None, _stream())
     pgq.check(rc, "pgq_dequant_codes")
     return out
+
+
+def qgemm(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X What^T with What = bf16(code * s) formed inside the GEMM.  x: bf16 [M, K] (rows
+    contiguous), codes: int8 [N, K], scales: fp16 bit patterns [N] (int16); returns fp32 [M, N]."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    assert codes.dtype == torch.int8 and codes.dim() == 2 and codes.stride(1) == 1
+    M, K = x.shape
+    N = codes.shape[0]
+    assert codes.shape[1] == K and scales.numel() == N and scales.is_contiguous()
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.float32, device=x.device)
+    rc = pgq.pgq_qgemm_bf16(_p(x), M, K, x.stride(0) if M > 1 else K, _p(codes), codes.stride(0) if N > 1 else K,
+                            _p(scales), N, _p(out), out.stride(0) if M > 1 else N, _stream())
+    pgq.check(rc, "pgq_qgemm_bf16")
+    return out

@@ -94,6 +94,7 @@ SIGNATURES = {
     "pgq_sqwa_accumulate": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan),
                                    ctypes.POINTER(_P), _I32, _P, _SZ, _U32, _P, _P]),
     "pgq_dequant_codes": (_I32, [_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
+    "pgq_qgemm_bf16": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "pgq_dequant_model": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan), _P,
                                  ctypes.POINTER(_P), _P, _SZ, _U32, _P, _P]),
     "pgq_average_workspace": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(_SZ)]),
@@ -157,6 +158,10 @@ def pgq_export_model(t, n, plan, arena, dq_out, workspace, workspace_bytes, flag
 def pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status, stream):
     return _lib.pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status,
                                     stream)
+
+
+def pgq_qgemm_bf16(x, M, K, ldx, codes, ldc, scales, N, y, ldy, stream):
+    return _lib.pgq_qgemm_bf16(x, M, K, ldx, codes, ldc, scales, N, y, ldy, stream)
 
 
 def pgq_dequant_codes(codes, packed, rows, cols, scales, per_tensor, awq_mult, out, dev_status, stream):
