@@ -301,7 +301,7 @@ def test_sqwa_resume_equals_uninterrupted():
 
 
 # ---------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("cols", [700, 1536, 3000])
+@pytest.mark.parametrize("cols", [700, 1536, 2000, 3000])
 def test_select_every_rank_path(cols):
     """Exact order statistics for ranks on both sides of each select strategy (iterated maximum
     up to 8, candidate packing up to 64, radix above), on continuous rows, rows with heavy ties
