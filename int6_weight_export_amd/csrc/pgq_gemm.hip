@@ -54,8 +54,16 @@ __global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restri
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t m0 = (int64_t)blockIdx.y * kBM;
-    const int64_t n0 = (int64_t)blockIdx.x * kBN;
+    // Workgroups are dealt to the 8 XCDs round-robin (workgroup i to XCD i mod 8) and each XCD has
+    // its own L2, so consecutive tiles -- which share X rows -- are given to workgroups of the same
+    // XCD: tile = (i mod 8)-th contiguous eighth of the tiles, element i / 8 of it (a bijection).
+    const uint32_t gx = (uint32_t)((N + kBN - 1) / kBN);
+    const uint32_t total = gridDim.x;
+    const uint32_t wid = blockIdx.x;
+    const uint32_t xcd = wid % 8u, per = total / 8u, rem = total % 8u;
+    const uint32_t tile = (xcd < rem ? xcd * (per + 1u) : rem * (per + 1u) + (xcd - rem) * per) + wid / 8u;
+    const int64_t m0 = (int64_t)(tile / gx) * kBM;
+    const int64_t n0 = (int64_t)(tile % gx) * kBN;
     const int wm = (wave >> 1) * 64;
     const int wn = (wave & 1) * 64;
     // staging: thread t loads row t / 2, K elements 16 (t % 2) .. + 15 of the step
@@ -150,7 +158,9 @@ __global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restri
 int launch_qgemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
                  const uint16_t* scales, int64_t N, float* y, int64_t ldy, uint32_t flags, void* stream)
 {
-    const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
+    const uint64_t tiles = (uint64_t)((N + kBN - 1) / kBN) * (uint64_t)((M + kBM - 1) / kBM);
+    if (tiles > 0xFFFFFFFFull) return (int)hipErrorInvalidValue;
+    const dim3 grid((unsigned)tiles);
     void* args[] = {&x, &M, &K, &ldx, &codes, &ldc, &scales, &N, &y, &ldy, &flags};
     return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_kernel), grid, dim3(256), args, stream);
 }
