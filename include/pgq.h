@@ -16,7 +16,15 @@
  *     lm_head.weight) and int6 AWQ export: "12L 24min Vocab1792 ... Int6AWQ MixedBits"
  *     (PR #1495), Submission summary and Mixed-bit quantization details;
  *   - averaging of quantize-dequantize snapshots (SQWA): "Discriminative TTT + SLOT-24"
- *     card (PR #1414), Novel Contributions.
+ *     card (PR #1414), Novel Contributions;
+ *   - EMA of the weights (decay 0.997): PR #1414 and "Unified Attention + FA3 + Legal TTT"
+ *     (PR #1202) cards, Weight Averaging; SWA over checkpoints: PR #69 card, Novel
+ *     Contributions and Weight Averaging;
+ *   - per-tensor scales: PR #2159 list (per-row / per-tensor quantization strategy);
+ *   - 6-bit code storage and its decode: the int6 artifact savings of the PR #69 card (the
+ *     byte layout is this library's own, documented at pgq_dequant_codes);
+ *   - the forward matmul over the STE-dequantized weights, dequantization fused: PR #69
+ *     card, section Other.
  *
  * The arithmetic, fixed where the pages leave it open (Q = 2^(bits-1) - 1, every step an
  * IEEE binary32 operation with round-to-nearest-even):
@@ -221,6 +229,8 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
 /* ------------------------------------------------------------------------------------------ */
 /* Decode stored codes back to fp32 weights (the artifact loader): x = code * s, divided by     */
 /* a_j when awq_mult is given -- bit for bit the dequantized value the export produced.        */
+/* Source: the int6 artifact savings of the "SubSixteen v2" card (PR #69), Novel              */
+/* Contributions; the pages give no byte layout, so the 6-bit layout below is ours.           */
 /*   codes      device, rows x cols int8 (packed = 0) or rows x 3 * ceil(cols / 4) bytes        */
 /*              (packed = 1): per row, group g of three bytes is the little-endian 24-bit word  */
 /*              holding codes 4g .. 4g+3 as 6-bit two's complement fields, code 4g + t in bits  */
