@@ -48,7 +48,7 @@ int awq_groups_per_wave()
 // Export tiles per workgroup of a whole-tensor select pass.
 int sel_group()
 {
-    static const int v = env_int("PGQ_SEL_GROUP", 2, 1, 64);   // measured best of 1, 2, 4, 8
+    static const int v = env_int("PGQ_SEL_GROUP", 3, 1, 64);   // measured best of 1, 2, 3, 4, 8
     return v;
 }
 
