@@ -2,26 +2,34 @@
 
     python -m int6_weight_export_amd.build          # or build_library() from Python
 
+Every translation unit is compiled to an object in parallel (the kernel instantiations are
+spread over several units for that reason), then the objects are linked.  Objects go to
+`_build/` next to this file; `incremental=True` reuses an object that is newer than its
+source and every header.
+
 Flags: strict IEEE binary32 (no FMA contraction, no fast-math, correctly rounded
 divide/sqrt, fp32 denormals kept) because outputs are compared bit for bit; packed
 fp32 instructions disabled.
 """
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpgq.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("pgq_api.hip", "pgq_kernels.hip", "pgq_gemm.hip")]
-HEADERS = [os.path.join(HERE, "csrc", "pgq_desc.h"), os.path.join(ROOT, "include", "pgq.h")]
+OBJ_DIR = os.path.join(HERE, "_build")
+SOURCES = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+HEADERS = sorted(glob.glob(os.path.join(HERE, "csrc", "*.h"))) + [os.path.join(ROOT, "include", "pgq.h")]
 ARCH = os.environ.get("PGQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -36,9 +44,32 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libpgq")
 
 
-def build_library(verbose: bool = False) -> str:
+def _jobs() -> int:
+    env = os.environ.get("MAX_JOBS")
+    n = int(env) if env and env.isdigit() else (os.cpu_count() or 4)
+    return max(1, min(n, 16, len(SOURCES)))
+
+
+def _compile(src: str, incremental: bool, verbose: bool) -> str:
+    obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
+    if incremental and os.path.exists(obj):
+        newest = max(os.path.getmtime(p) for p in [src, *HEADERS, __file__])
+        if os.path.getmtime(obj) > newest:
+            return obj
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj + ".tmp", src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(obj + ".tmp", obj)
+    return obj
+
+
+def build_library(verbose: bool = False, incremental: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with ThreadPoolExecutor(_jobs()) as pool:
+        objs = list(pool.map(lambda s: _compile(s, incremental, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SOURCES]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
@@ -47,4 +78,4 @@ def build_library(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv))
+    print(build_library(verbose="-v" in sys.argv, incremental="-i" in sys.argv))

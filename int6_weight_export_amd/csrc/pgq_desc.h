@@ -132,6 +132,22 @@ int launch_decode(const void* codes, int32_t packed, int64_t rows, int64_t cols,
 // The final pick of the whole-tensor selects: one workgroup per descriptor.
 int launch_tensor_pick(const KArgs& ka, uint32_t n_desc, void* stream);
 
+// Kernel instantiations for a variant v = variant_of(mode, need), grouped by mode into translation
+// units of their own (pgq_k_*.hip) so that they compile in parallel; null when none exists.
+// Export-like modes: kernels_<mode> holds the lean streaming variants, kernels_<mode>_sel the
+// percentile-select variant, kernels_<mode>_all_* the variant with every feature.
+#define PGQ_EXPORT_LIKE_PARTS(m)                                \
+    const void* kernels_##m(uint32_t v, bool table);             \
+    const void* kernels_##m##_sel(bool table);                   \
+    const void* kernels_##m##_all_table();                       \
+    const void* kernels_##m##_all_single();
+PGQ_EXPORT_LIKE_PARTS(export)
+PGQ_EXPORT_LIKE_PARTS(export6)
+PGQ_EXPORT_LIKE_PARTS(sqwa)
+#undef PGQ_EXPORT_LIKE_PARTS
+const void* kernels_fq(int mode, uint32_t v, bool table);
+const void* kernels_avg(int mode, uint32_t v, bool table);
+
 // Register tile: a row of up to 64 * chunks * elements stays in VGPRs; longer rows stream.
 constexpr int64_t kRegCols_F32 = 64 * 8 * 4;     // 2048
 constexpr int64_t kRegCols_BF16 = 64 * 4 * 8;    // 2048
