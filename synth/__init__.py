@@ -22,6 +22,7 @@ from .weights import (  # noqa: F401
     config4,
     config5_base,
     config5_snapshot,
+    config5_snapshots,
     stress_s1,
     stress_s2,
     stress_s4_weights,

@@ -130,9 +130,19 @@ class SynthTensor:
 SIGMA_W = 0.02
 
 
-def config1_batch(count: int) -> List[SynthTensor]:
+def _map(fn, items, workers: int):
+    """[fn(x) for x in items], on `workers` threads (numpy releases the GIL in the array work)."""
+    if workers <= 1:
+        return [fn(x) for x in items]
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(workers) as pool:
+        return list(pool.map(fn, items))
+
+
+def config1_batch(count: int, workers: int = 1) -> List[SynthTensor]:
     """`count` independent fp32 1536x512 matrices, N(0, 0.02^2), seeds 0..count-1."""
-    return [SynthTensor(f"mat{b}", gauss_f32(key_of(1, b), (1536, 512), SIGMA_W)) for b in range(count)]
+    return _map(lambda b: SynthTensor(f"mat{b}", gauss_f32(key_of(1, b), (1536, 512), SIGMA_W)), range(count), workers)
 
 
 def config1() -> SynthTensor:
@@ -223,6 +233,12 @@ def config5_snapshot(k: int, base: Optional[List[SynthTensor]] = None) -> List[S
     base = base if base is not None else config5_base()
     return [SynthTensor(t.name, gauss_f32(key_of(5, i, k), t.shape, 0.002 * k, mean=t.data))
             for i, t in enumerate(base)]
+
+
+def config5_snapshots(ks, base: Optional[List[SynthTensor]] = None, workers: int = 1) -> List[List[SynthTensor]]:
+    """config5_snapshot(k, base) for every k in ks."""
+    base = base if base is not None else config5_base()
+    return _map(lambda k: config5_snapshot(k, base), list(ks), workers)
 
 
 def stress_s1() -> List[SynthTensor]:
