@@ -4,24 +4,37 @@
 // STE fake quantization runs in the forward pass ("SubSixteen v2" card, PR #69, section Other):
 // the layer's matmul consumes What[n][k] = bf16(fp32(code[n][k] * s_n)), the STE forward's
 // dequantized weight.  Here the matmul reads the int8 codes and fp16 row scales instead of a
-// materialised bf16 What, forms each bf16 weight in registers on its way into LDS, and runs
-// the contraction on the matrix cores:
+// materialised bf16 What, forms each bf16 weight in registers, and runs the contraction on the
+// matrix cores:
 //
 //     Y[m][n] = sum_k X[m][k] * What[n][k]      X bf16 [M x K], Y fp32 [M x N]
 //
 // Each product of two bf16 values is exact in fp32; the MFMA accumulates in fp32.
 //
-// Tiling: a workgroup of four wavefronts computes a 128 x 128 tile of Y; each wavefront a
-// 64 x 64 quarter as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Per 32-wide K step the
-// workgroup stages X[128 x 32] and What[128 x 32] in LDS (rows padded to 40 halves), every
-// thread loading 16 consecutive K elements of one row.  Operand layout of the instruction
-// (checked on the device): lane l supplies row l % 32 of A (and column l % 32 of B) with
-// k = 8 (l / 32) + i, i = 0..7; accumulator register j of lane l is row 8 (j / 4) +
-// 4 (l / 32) + j % 4, column l % 32.
+// Two kernels.  The main one (pgq_qgemm_kernel) takes 16-byte loadable rows and K a multiple of
+// 16: a workgroup of four wavefronts computes a 128 x 128 tile of Y, each wavefront a 64 x 64
+// quarter as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  X[128 x 64] and the raw int8
+// codes[128 x 64] of each 64-wide K step go from global memory straight into LDS (buffer loads
+// with the LDS destination, no registers on the way), into a ring of kStages buffers, so the
+// loads of the next steps are in flight while the matrix cores work on this one; a lane past
+// M, N or K gets zeros from the buffer range check.  Each wavefront turns its own code
+// fragments into bf16(code * s_n) in registers.  The generic kernel
+// (pgq_qgemm_generic_kernel) takes any shape: element loads through registers into LDS.
+//
+// Operand layout of the instruction (checked on the device): lane l supplies row l % 32 of A
+// (and column l % 32 of B) with 8 consecutive k, the lanes 32..63 the next 8; accumulator
+// register j of lane l is row 8 (j / 4) + 4 (l / 32) + j % 4, column l % 32.  Which of the
+// tile's k a lane half supplies in which instruction is free as long as A and B agree: in the
+// main kernel, lane half h supplies k = 16 h + 8 t .. + 7 of a 32-wide block in the block's
+// t-th instruction, so that a lane reads its 16 contiguous k of each row with one LDS read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "pgq_desc.h"
+
+#ifndef PGQ_QGEMM_STAGES
+#define PGQ_QGEMM_STAGES 2
+#endif
 
 namespace pgq {
 namespace {
@@ -44,7 +57,7 @@ __device__ __forceinline__ uint16_t to_bf16(float f)
 
 // flags: bit 0 = X rows are 16-byte loadable (ldx % 8 == 0, X 16-byte aligned),
 //        bit 1 = code rows are 16-byte loadable (ldc % 16 == 0, codes 16-byte aligned)
-__global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+__global__ void __launch_bounds__(256) pgq_qgemm_generic_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        int64_t ldx, const int8_t* __restrict__ codes, int64_t ldc,
                                                        const uint16_t* __restrict__ scales, int64_t N,
                                                        float* __restrict__ y, int64_t ldy, uint32_t flags)
@@ -71,7 +84,7 @@ __global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restri
     const int lk = (tid & 1) * 16;
     const int64_t am = m0 + lr;
     const int64_t bn = n0 + lr;
-    const float sb = bn < N ? half_to_float(scales[bn]) : 0.0f;
+    const float sb = (K > 0 && bn < N) ? half_to_float(scales[bn]) : 0.0f;   // K = 0: nothing is read
     const bool xvec = (flags & 1u) != 0;
     const bool cvec = (flags & 2u) != 0;
 
@@ -153,16 +166,230 @@ __global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restri
         }
 }
 
+
+// ---- main kernel: direct-to-LDS loads into a ring of stages ---------------------------------------
+constexpr int kTK = 64;                        // K per stage
+constexpr int kStages = PGQ_QGEMM_STAGES;
+constexpr int kAStage = 128 * kTK * 2;         // X bytes per stage (128 rows x 128 B)
+constexpr int kBStage = 128 * kTK;             // code bytes per stage (128 rows x 64 B)
+constexpr uint32_t kOOB = 0x80000000u;         // a buffer offset past every range: the load returns 0
+
+// LDS slots are 16-byte granules.  X rows hold 8 granules, code rows 4; granule g of row r is
+// stored in slot g ^ swz(r) of the row, so that the 32 rows a fragment read touches (same
+// granule) spread over distinct banks in every group of 8 and of 16 lanes.
+__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_b(int r) { return (((r >> 1) & 1) ^ ((r >> 3) & 1)) | (((r >> 2) & 1) << 1); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// one wave's share of one stage's loads: 4 X instructions, 2 code instructions, each 64 lanes x 16
+// bytes into 1 KB of consecutive LDS; voff: the lanes' byte offsets (kOOB for zeros)
+__device__ __forceinline__ void stage_loads(__amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t cr, uint8_t* lds_a,
+                                            uint8_t* lds_b, int wave, const uint32_t (&xo)[4], const uint32_t (&co)[2])
+{
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(lds_a + (c * 256 + wave * 64) * 16), 16, xo[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr)(lds_b + (c * 256 + wave * 64) * 16), 16, co[c], 0, 0, 0);
+}
+
+// vmcnt(n) for the few n the pipeline needs (an immediate operand)
+__device__ __forceinline__ void wait_vm(int n)
+{
+    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n <= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+}
+
+// every wave's LDS reads are complete, then the workgroup barrier (the asm keeps the compiler
+// from moving memory operations across it)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 16 int8 codes (one 16-byte LDS granule) -> two bf16x8 fragments of bf16(code * s): with
+// u = byte + 128 from the biased byte, fma(u, s, -128 s) = code * s exactly (at most 7 + 11
+// significant bits), then round to bf16
+__device__ __forceinline__ void codes_to_bf16(u32x4 q, float s, float s128, bf16x8& lo, bf16x8& hi)
+{
+    float v[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t b = q[w] ^ 0x80808080u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * w + e] = __builtin_fmaf((float)((b >> (8 * e)) & 0xFFu), s, s128);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        lo[e] = (__bf16)v[e];
+        hi[e] = (__bf16)v[8 + e];
+    }
+}
+
+__global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                       int64_t ldx, const int8_t* __restrict__ codes, int64_t ldc,
+                                                       const uint16_t* __restrict__ scales, int64_t N,
+                                                       float* __restrict__ y, int64_t ldy)
+{
+    __shared__ __align__(16) uint8_t lds[kStages * (kAStage + kBStage)];
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // tiles sharing X rows go to workgroups of one XCD (workgroup i runs on XCD i mod 8)
+    const uint32_t gx = (uint32_t)((N + 127) / 128);
+    const uint32_t total = gridDim.x;
+    const uint32_t wid = blockIdx.x;
+    const uint32_t xcd = wid % 8u, per = total / 8u, rem = total % 8u;
+    const uint32_t tile = (xcd < rem ? xcd * (per + 1u) : rem * (per + 1u) + (xcd - rem) * per) + wid / 8u;
+    const int64_t m0 = (int64_t)(tile / gx) * 128;
+    const int64_t n0 = (int64_t)(tile % gx) * 128;
+    const int mrows = (int)min((int64_t)128, M - m0);
+    const int nrows = (int)min((int64_t)128, N - n0);
+    // buffer ranges over this tile's rows (at most 128 rows: the host keeps them below 2^31 bytes)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + m0 * ldx), 0, (int)((int64_t)mrows * ldx * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(codes + n0 * ldc), 0, (int)((int64_t)nrows * ldc), 0x00020000);
+
+    // this lane's load slots: X instruction c covers slot p = 256 c + tid (row p / 8, slot p % 8),
+    // codes instruction c slot p = 256 c + tid (row p / 4, slot p % 4); the granule loaded into a
+    // slot is slot ^ swz(row)
+    uint32_t xbase[4], cbase[2];
+    int xk[4], ck[2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int p = 256 * c + tid, r = p >> 3, g = (p & 7) ^ swz_a(r);
+        xk[c] = 8 * g;
+        xbase[c] = r < mrows ? (uint32_t)(r * ldx + 8 * g) * 2u : kOOB;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int p = 256 * c + tid, r = p >> 2, g = (p & 3) ^ swz_b(r);
+        ck[c] = 16 * g;
+        cbase[c] = r < nrows ? (uint32_t)(r * ldc + 16 * g) : kOOB;
+    }
+    const int nst = (int)((K + kTK - 1) / kTK);
+    auto issue = [&](int st) {
+        const int k0 = st * kTK;
+        uint32_t xo[4], co[2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xo[c] = (xbase[c] != kOOB && k0 + xk[c] < K) ? xbase[c] + (uint32_t)k0 * 2u : kOOB;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) co[c] = (cbase[c] != kOOB && k0 + ck[c] < K) ? cbase[c] + (uint32_t)k0 : kOOB;
+        uint8_t* base = lds + (st % kStages) * (kAStage + kBStage);
+        stage_loads(xr, cr, base, base + kAStage, wave, xo, co);
+    };
+
+    const int wm = (wave >> 1) * 64;
+    const int wn = (wave & 1) * 64;
+    const int r32 = lane & 31;
+    const int h = lane >> 5;
+    // the scales of this lane's two weight rows (columns of Y)
+    float sc[2], sc128[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wn + 32 * j + r32;
+        sc[j] = n < N ? half_to_float(scales[n]) : 0.0f;
+        sc128[j] = -128.0f * sc[j];                      // exact
+    }
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    // one 32-wide K block of the stage at la / lb: 8 MFMAs per wavefront
+    auto block = [&](const uint8_t* la, const uint8_t* lb, int kb) {
+        bf16x8 fa[2][2];                                 // [i][t]
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = wm + 32 * i + r32;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int g = 4 * kb + 2 * h + t;
+                fa[i][t] = *reinterpret_cast<const bf16x8*>(la + (r * 8 + (g ^ swz_a(r))) * 16);
+            }
+        }
+        bf16x8 fb[2][2];                                 // [j][t]
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = wn + 32 * j + r32;
+            const int g = 2 * kb + h;
+            const u32x4 q = *reinterpret_cast<const u32x4*>(lb + (r * 4 + (g ^ swz_b(r))) * 16);
+            codes_to_bf16(q, sc[j], sc128[j], fb[j][0], fb[j][1]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
+    };
+    // stage st: wait for its loads (the later stages already issued may stay in flight), then the
+    // barrier after which every wave's loads of st are in LDS and every wave is done reading the
+    // buffer of st - 1, which the next stage's loads then reuse
+    auto enter = [&](int st) {
+        wait_vm(6 * (min(nst, st + kStages - 1) - st - 1));
+        lds_barrier();
+        if (st + kStages - 1 < nst) issue(st + kStages - 1);
+    };
+    auto stage_lds = [&](int st) { return lds + (st % kStages) * (kAStage + kBStage); };
+
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st)
+        if (st < nst) issue(st);
+    const int nfull = (int)(K / kTK);                    // stages with both 32-wide blocks in range
+    for (int st = 0; st < nfull; ++st) {
+        enter(st);
+        const uint8_t* la = stage_lds(st);
+        block(la, la + kAStage, 0);
+        block(la, la + kAStage, 1);
+    }
+    const int ktail = (int)(K % kTK);                    // 0, 16, 32 or 48
+    if (ktail) {
+        enter(nfull);
+        const uint8_t* la = stage_lds(nfull);
+        block(la, la + kAStage, 0);
+        if (ktail > 32) block(la, la + kAStage, 1);
+    }
+
+    // Y is written once and never read here: non-temporal stores.  For register r, lanes 0..31
+    // hold 32 consecutive columns of one row and lanes 32..63 those of the row 4 below.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = n0 + wn + 32 * j + r32;
+            if (col < N) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (row < M) __builtin_nontemporal_store(acc[i][j][r], (GLB float*)y + row * ldy + col);
+                }
+            }
+        }
+}
+
 }  // namespace
 
 int launch_qgemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
                  const uint16_t* scales, int64_t N, float* y, int64_t ldy, uint32_t flags, void* stream)
 {
-    const uint64_t tiles = (uint64_t)((N + kBN - 1) / kBN) * (uint64_t)((M + kBM - 1) / kBM);
+    const uint64_t tiles = (uint64_t)((N + 127) / 128) * (uint64_t)((M + 127) / 128);
     if (tiles > 0xFFFFFFFFull) return (int)hipErrorInvalidValue;
     const dim3 grid((unsigned)tiles);
+    // the main kernel: 16-byte loadable X and code rows, K a positive multiple of 16, and a tile's
+    // 128 rows of either operand within a 32-bit buffer range
+    const bool main = (flags & 3u) == 3u && K > 0 && K % 16 == 0 && ldx < ((int64_t)1 << 22) &&
+                      ldc < ((int64_t)1 << 23);
+    if (main) {
+        void* args[] = {&x, &M, &K, &ldx, &codes, &ldc, &scales, &N, &y, &ldy};
+        return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_kernel), grid, dim3(256), args, stream);
+    }
     void* args[] = {&x, &M, &K, &ldx, &codes, &ldc, &scales, &N, &y, &ldy, &flags};
-    return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_kernel), grid, dim3(256), args, stream);
+    return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_generic_kernel), grid, dim3(256), args, stream);
 }
 
 }  // namespace pgq

@@ -311,3 +311,46 @@ def test_dequant_model_argument_errors():
     outs[1] = FAKE
     plan[0].kind = 9
     assert dm(arr, 4, plan, FAKE, outs, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM
+
+
+def test_qgemm_argument_errors():
+    g = pgq.pgq_qgemm_bf16
+    # (x, M, K, ldx, codes, ldc, scales, N, y, ldy, stream)
+    ok = dict(x=FAKE, M=4, K=32, ldx=32, codes=FAKE, ldc=32, scales=FAKE, N=8, y=FAKE, ldy=8)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return g(a["x"], a["M"], a["K"], a["ldx"], a["codes"], a["ldc"], a["scales"], a["N"], a["y"], a["ldy"], None)
+
+    assert call(M=-1) == pgq.PGQ_ERR_SHAPE
+    assert call(N=-1) == pgq.PGQ_ERR_SHAPE
+    assert call(K=-1) == pgq.PGQ_ERR_SHAPE
+    assert call(ldx=31) == pgq.PGQ_ERR_SHAPE
+    assert call(ldc=31) == pgq.PGQ_ERR_SHAPE
+    assert call(ldy=7) == pgq.PGQ_ERR_SHAPE
+    assert call(M=0) == pgq.PGQ_OK                     # nothing to do, nothing enqueued
+    assert call(N=0) == pgq.PGQ_OK
+    assert call(y=None) == pgq.PGQ_ERR_NULL
+    assert call(x=None) == pgq.PGQ_ERR_NULL
+    assert call(codes=None) == pgq.PGQ_ERR_NULL
+    assert call(scales=None) == pgq.PGQ_ERR_NULL
+    assert call(x=FAKE + 1) == pgq.PGQ_ERR_ALIGN
+    assert call(scales=FAKE + 1) == pgq.PGQ_ERR_ALIGN
+    assert call(y=FAKE + 2) == pgq.PGQ_ERR_ALIGN
+
+
+def test_per_tensor_export_without_weights_is_refused():
+    """A per-tensor export descriptor must carry its weights (the whole-tensor select reads them):
+    the host refuses a NULL weight pointer before anything is enqueued."""
+    ts = synth.config2()[:9]
+    arr, keep = _tensor_array(ts)
+    pol, k2 = _policy()
+    pol.per_tensor = 1
+    plan = (pgq.pgq_tensor_plan * 9)()
+    ab, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert pgq.pgq_export_plan(arr, 9, ctypes.byref(pol), plan, ctypes.byref(ab), ctypes.byref(wb)) == 0
+    assert any(plan[i].per_tensor for i in range(9))
+    i = next(i for i in range(9) if plan[i].per_tensor)
+    arr[i].w = None
+    assert pgq.pgq_export_model(arr, 9, plan, FAKE, None, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_NULL

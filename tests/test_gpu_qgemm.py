@@ -47,8 +47,11 @@ def _check(y, x, codes, scales, rows=None, what=""):
     assert np.all(err <= tol), f"{what}: max err {err.max()} vs tol {tol[err > tol].min()}"
 
 
+# K a multiple of 16 with 16-byte rows takes the direct-to-LDS kernel (K % 64 = 0, 16, 32, 48 cover
+# its tail stage; K = 16 has no full stage); the others take the generic kernel
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (5, 7, 3), (129, 130, 33), (64, 128, 32), (200, 1584, 528),
-                                   (300, 528, 1584), (131, 257, 100)])
+                                   (300, 528, 1584), (131, 257, 100), (1, 1, 16), (3, 5, 48), (130, 129, 64),
+                                   (257, 300, 80), (520, 390, 1040), (128, 128, 2048), (384, 260, 176)])
 def test_qgemm_small_and_ragged(M, N, K):
     say(f"qgemm {M}x{N}x{K}")
     x, codes, scales = _inputs(M, N, K, M + N + K)
@@ -93,3 +96,35 @@ def test_qgemm_uses_the_fake_quant_outputs_on_device():
     torch.cuda.synchronize()
     ref = oracle.fakequant_rows(w, 31)
     _check(y.cpu().numpy(), x, ref["codes"], ref["scales"], what="device fake quant")
+
+
+def test_qgemm_k_zero_writes_zeros_without_reading_operands():
+    """K = 0: Y = +0 everywhere, with x, codes and scales NULL (nothing is read)."""
+    from int6_weight_export_amd import pgq
+
+    say("qgemm K = 0 with NULL operands")
+    M, N = 70, 45
+    y = torch.full((M, N + 3), 7.0, dtype=torch.float32, device="cuda")
+    rc = pgq.pgq_qgemm_bf16(None, M, 0, 0, None, 0, None, N, y.data_ptr(), N + 3,
+                            torch.cuda.current_stream().cuda_stream)
+    assert rc == pgq.PGQ_OK
+    torch.cuda.synchronize()
+    yy = y.cpu().numpy()
+    assert np.all(yy[:, :N].view(np.uint32) == 0)        # +0, sign included
+    assert np.all(yy[:, N:] == 7.0)
+
+
+def test_qgemm_bench_shape_sampled_rows_and_repeatable():
+    """16384 x 1584 x 528, the timed workload: sampled rows from every region of the output
+    (first and last row tiles, the ragged last column tile), and bit-identical on a second run."""
+    say("qgemm 16384 x 1584 x 528 sampled rows, repeat")
+    M, N, K = 16384, 1584, 528
+    x, codes, scales = _inputs(M, N, K, 17)
+    xd, cd, sd = _bf16(x), torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda()
+    y1 = ops.qgemm(xd, cd, sd)
+    y2 = ops.qgemm(xd, cd, sd)
+    torch.cuda.synchronize()
+    a, b = y1.cpu().numpy(), y2.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    rows = np.r_[0:2, 126:131, 8000:8002, 16255:16258, 16382:16384]
+    _check(a, x, codes, scales, rows=rows, what="bench shape")
