@@ -773,6 +773,7 @@ pgq_status pgq_qgemm_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
     uint32_t f = 0;
     if (x && ldx % 8 == 0 && aligned(x, 16)) f |= 1u;
     if (codes && ldc % 16 == 0 && aligned(codes, 16)) f |= 2u;
+    if (ldy % 4 == 0 && aligned(y, 16)) f |= 4u;
     if (const int e = launch_qgemm(x, M, K, ldx, codes, ldc, scales, N, y, ldy, f, stream)) return hip_failed((hipError_t)e);
     if (const hipError_t e = hipGetLastError()) return hip_failed(e);
     return PGQ_OK;

@@ -20,9 +20,10 @@ enum Mode : int32_t {
     MODE_TSEL = 6,    // one pass of the whole-tensor clip select (per-tensor scales)
     MODE_EXPORT6 = 7, // export whose int6 codes are stored 4 per 3 bytes (a separate build of the
                       // export kernels, so the plain export keeps its register budget)
-    MODE_DECODE = 8   // stored artifact (codes / packed codes / fp16) back to fp32
+    MODE_DECODE = 8,  // stored artifact (codes / packed codes / fp16) back to fp32
+    MODE_TCAND = 9    // whole-tensor clip, one read: every workgroup emits its candidate keys
 };
-constexpr int kModes = 9;
+constexpr int kModes = 10;
 template <int M>
 constexpr bool is_export = M == MODE_EXPORT || M == MODE_EXPORT6;
 enum : int32_t { IN_F32 = 0, IN_BF16 = 1 };
@@ -30,7 +31,9 @@ enum : int32_t { KIND_F16 = 16 };
 enum : uint32_t {
     DF_VEC = 1u,          // 16-byte vector path allowed for this tensor
     DF_TENSOR = 2u,       // one scale for the whole tensor, clip from its TState
-    DF_PACK6 = 4u         // codes stored 4 per 3 bytes (6-bit fields), 3 * ceil(cols / 4) per row
+    DF_PACK6 = 4u,        // codes stored 4 per 3 bytes (6-bit fields), 3 * ceil(cols / 4) per row
+    DF_CAND = 8u          // DF_TENSOR clip found from candidate keys (MODE_TCAND) instead of the
+                          // radix passes (MODE_TSEL)
 };
 
 // Features a launch needs; each kernel instantiation covers a fixed set of them, and the
@@ -47,16 +50,21 @@ enum : uint32_t {
     F_ALL = 127u
 };
 
-// State of one tensor's whole-tensor clip select, in the caller's workspace.  Pass p of the
-// radix select adds every workgroup's LDS histogram of key digit p (bits 30..23, 22..15, 14..7,
-// 6..0 of |x|, among the keys matching the digits already chosen) into hist[p]; the digits
-// chosen so far are re-derived from hist[0 .. p-1] by whoever needs them.  The final pick
-// stores the selected key and zeroes hist / kmax, so consecutive calls need no reset.
+// State of one tensor's whole-tensor clip select, in the caller's workspace.
+// Candidate select (DF_CAND, one read of the tensor): every workgroup of the MODE_TCAND launch
+// appends the keys of its rows that can still be the clip to the tensor's candidate array
+// (Desc::cand), taking its place with an atomic add on ncand; the pick ranks them.
+// Radix select: pass p adds every workgroup's LDS histogram of key digit p (bits 30..23,
+// 22..15, 14..7, 6..0 of |x|, among the keys matching the digits already chosen) into hist[p];
+// the digits chosen so far are re-derived from hist[0 .. p-1] by whoever needs them.
+// The final pick stores the selected key and zeroes hist / kmax / ncand, so consecutive calls
+// need no reset.
 struct alignas(64) TState {
     uint32_t hist[4][256];
     uint32_t kmax;        // absmax select: running maximum key
     uint32_t key;         // the selected |x| bit pattern, read by the quantize pass
-    uint32_t pad[14];
+    uint32_t ncand;       // candidate select: keys appended so far
+    uint32_t pad[13];
 };
 
 struct alignas(16) Desc {
@@ -82,6 +90,9 @@ struct alignas(16) Desc {
     int32_t rgroup;           // rows a wave processes together (1, 2, 4 or 8)
     int32_t tile_rows;        // rows per tile: kWaves * rgroup * groups per wave
     int32_t nch;              // vector path: ceil(chunks / 64) per row, 0 when the row streams
+    uint32_t* cand;           // DF_CAND: candidate keys (workspace), ctiles * ccap entries
+    int32_t crows;            // DF_CAND: rows per candidate tile (kWaves * rows per wave)
+    int32_t ccap;             // DF_CAND: most keys a candidate tile appends
 };
 
 struct alignas(64) TableHeader {
@@ -123,7 +134,8 @@ void set_timing_events(void* start, void* stop);
 void take_timing_events(void** start, void** stop);
 // Any kernel with a 3-D grid, taking a pending timing-event pair like the others.
 hipError_t launch_plain(const void* fn, dim3 grid, dim3 block, void** args, void* stream);
-// The fused-dequant GEMM (pgq_gemm.hip); flags: bit 0 X rows 16-byte loadable, bit 1 code rows.
+// The fused-dequant GEMM (pgq_gemm.hip); flags: bit 0 X rows 16-byte loadable, bit 1 code rows,
+// bit 2 Y rows 16-byte aligned.
 int launch_qgemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
                  const uint16_t* scales, int64_t N, float* y, int64_t ldy, uint32_t flags, void* stream);
 // Decode of stored codes to fp32 (rows > 0, cols > 0).

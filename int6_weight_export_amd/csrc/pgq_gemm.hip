@@ -12,14 +12,14 @@
 // Each product of two bf16 values is exact in fp32; the MFMA accumulates in fp32.
 //
 // Two kernels.  The main one (pgq_qgemm_kernel) takes 16-byte loadable rows and K a multiple of
-// 16: a workgroup of four wavefronts computes a 128 x 128 tile of Y, each wavefront a 64 x 64
-// quarter as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  X[128 x 64] and the raw int8
-// codes[128 x 64] of each 64-wide K step go from global memory straight into LDS (buffer loads
-// with the LDS destination, no registers on the way), into a ring of kStages buffers, so the
-// loads of the next steps are in flight while the matrix cores work on this one; a lane past
-// M, N or K gets zeros from the buffer range check.  Each wavefront turns its own code
-// fragments into bf16(code * s_n) in registers.  The generic kernel
-// (pgq_qgemm_generic_kernel) takes any shape: element loads through registers into LDS.
+// 16: a workgroup of four wavefronts computes a 256 x 128 tile of Y, each wavefront a 128 x 64
+// part as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.  X[256 x 64] and the raw int8 codes[128 x 64]
+// of each 64-wide K step go from global memory straight into LDS (buffer loads with the LDS
+// destination, no registers on the way), double-buffered, so the next step's loads are in
+// flight while the matrix cores work on this one; a lane past M, N or K gets zeros from the
+// buffer range check.  Each wavefront turns its own code fragments into bf16(code * s_n) in
+// registers.  Y leaves through an LDS transpose as 16-byte non-temporal stores.  The generic
+// kernel (pgq_qgemm_generic_kernel) takes any shape: element loads through registers into LDS.
 //
 // Operand layout of the instruction (checked on the device): lane l supplies row l % 32 of A
 // (and column l % 32 of B) with 8 consecutive k, the lanes 32..63 the next 8; accumulator
@@ -32,9 +32,6 @@
 
 #include "pgq_desc.h"
 
-#ifndef PGQ_QGEMM_STAGES
-#define PGQ_QGEMM_STAGES 2
-#endif
 
 namespace pgq {
 namespace {
@@ -167,11 +164,14 @@ __global__ void __launch_bounds__(256) pgq_qgemm_generic_kernel(const uint16_t* 
 }
 
 
-// ---- main kernel: direct-to-LDS loads into a ring of stages ---------------------------------------
+// ---- main kernel: direct-to-LDS loads, double-buffered ---------------------------------------------
 constexpr int kTK = 64;                        // K per stage
-constexpr int kStages = PGQ_QGEMM_STAGES;
-constexpr int kAStage = 128 * kTK * 2;         // X bytes per stage (128 rows x 128 B)
-constexpr int kBStage = 128 * kTK;             // code bytes per stage (128 rows x 64 B)
+constexpr int kIB = 4;                         // 32-row MFMA blocks per wavefront
+constexpr int kTM = 64 * kIB;                  // workgroup rows (2 wavefronts along M): 256
+constexpr int kTN = 128;                       // workgroup columns (2 wavefronts along N)
+constexpr int kXI = kTM / 32;                  // X load instructions per thread per stage
+constexpr int kAS = kTM * kTK * 2;             // X bytes per stage (256 rows x 128 B)
+constexpr int kBS = kTN * kTK;                 // code bytes per stage (128 rows x 64 B)
 constexpr uint32_t kOOB = 0x80000000u;         // a buffer offset past every range: the load returns 0
 
 // LDS slots are 16-byte granules.  X rows hold 8 granules, code rows 4; granule g of row r is
@@ -181,31 +181,18 @@ __device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_b(int r) { return (((r >> 1) & 1) ^ ((r >> 3) & 1)) | (((r >> 2) & 1) << 1); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// one wave's share of one stage's loads: 4 X instructions, 2 code instructions, each 64 lanes x 16
-// bytes into 1 KB of consecutive LDS; voff: the lanes' byte offsets (kOOB for zeros)
-__device__ __forceinline__ void stage_loads(__amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t cr, uint8_t* lds_a,
-                                            uint8_t* lds_b, int wave, const uint32_t (&xo)[4], const uint32_t (&co)[2])
-{
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(lds_a + (c * 256 + wave * 64) * 16), 16, xo[c], 0, 0, 0);
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr)(lds_b + (c * 256 + wave * 64) * 16), 16, co[c], 0, 0, 0);
-}
-
-// vmcnt(n) for the few n the pipeline needs (an immediate operand)
-__device__ __forceinline__ void wait_vm(int n)
-{
-    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (n <= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // every wave's LDS reads are complete, then the workgroup barrier (the asm keeps the compiler
 // from moving memory operations across it)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));   // round to nearest even
+}
 
 // 16 int8 codes (one 16-byte LDS granule) -> two bf16x8 fragments of bf16(code * s): with
 // u = byte + 128 from the biased byte, fma(u, s, -128 s) = code * s exactly (at most 7 + 11
@@ -219,68 +206,80 @@ __device__ __forceinline__ void codes_to_bf16(u32x4 q, float s, float s128, bf16
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * w + e] = __builtin_fmaf((float)((b >> (8 * e)) & 0xFFu), s, s128);
     }
+    u32x4 a, c;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        lo[e] = (__bf16)v[e];
-        hi[e] = (__bf16)v[8 + e];
+    for (int e = 0; e < 4; ++e) {
+        a[e] = pk_bf16(v[2 * e], v[2 * e + 1]);
+        c[e] = pk_bf16(v[8 + 2 * e], v[8 + 2 * e + 1]);
     }
+    lo = __builtin_bit_cast(bf16x8, a);
+    hi = __builtin_bit_cast(bf16x8, c);
 }
 
-__global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                       int64_t ldx, const int8_t* __restrict__ codes, int64_t ldc,
-                                                       const uint16_t* __restrict__ scales, int64_t N,
-                                                       float* __restrict__ y, int64_t ldy)
+// A workgroup of four wavefronts computes a 256 x 128 tile of Y; wavefront w a 128 x 64 part
+// (rows 128 (w / 2), columns 64 (w % 2)) as 4 x 2 blocks of 32 x 32.  Occupancy floor of two
+// wavefronts per SIMD (the register budget the 128 accumulators leave), matching the two
+// workgroups per compute unit that the 80 KB of LDS allow.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const int8_t* __restrict__ codes,
+                 int64_t ldc, const uint16_t* __restrict__ scales, int64_t N, float* __restrict__ y, int64_t ldy)
 {
-    __shared__ __align__(16) uint8_t lds[kStages * (kAStage + kBStage)];
+    __shared__ __align__(16) uint8_t lds[2 * (kAS + kBS)];
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // tiles sharing X rows go to workgroups of one XCD (workgroup i runs on XCD i mod 8)
-    const uint32_t gx = (uint32_t)((N + 127) / 128);
+    const uint32_t gx = (uint32_t)((N + kTN - 1) / kTN);
     const uint32_t total = gridDim.x;
     const uint32_t wid = blockIdx.x;
     const uint32_t xcd = wid % 8u, per = total / 8u, rem = total % 8u;
     const uint32_t tile = (xcd < rem ? xcd * (per + 1u) : rem * (per + 1u) + (xcd - rem) * per) + wid / 8u;
-    const int64_t m0 = (int64_t)(tile / gx) * 128;
-    const int64_t n0 = (int64_t)(tile % gx) * 128;
-    const int mrows = (int)min((int64_t)128, M - m0);
-    const int nrows = (int)min((int64_t)128, N - n0);
-    // buffer ranges over this tile's rows (at most 128 rows: the host keeps them below 2^31 bytes)
+    const int64_t m0 = (int64_t)(tile / gx) * kTM;
+    const int64_t n0 = (int64_t)(tile % gx) * kTN;
+    const int mrows = (int)min((int64_t)kTM, M - m0);
+    const int nrows = (int)min((int64_t)kTN, N - n0);
+    // buffer ranges over this tile's rows (the host keeps them below 2^31 bytes)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(x + m0 * ldx), 0, (int)((int64_t)mrows * ldx * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(codes + n0 * ldc), 0, (int)((int64_t)nrows * ldc), 0x00020000);
 
-    // this lane's load slots: X instruction c covers slot p = 256 c + tid (row p / 8, slot p % 8),
-    // codes instruction c slot p = 256 c + tid (row p / 4, slot p % 4); the granule loaded into a
-    // slot is slot ^ swz(row)
-    uint32_t xbase[4], cbase[2];
-    int xk[4], ck[2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int p = 256 * c + tid, r = p >> 3, g = (p & 7) ^ swz_a(r);
-        xk[c] = 8 * g;
-        xbase[c] = r < mrows ? (uint32_t)(r * ldx + 8 * g) * 2u : kOOB;
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int p = 256 * c + tid, r = p >> 2, g = (p & 3) ^ swz_b(r);
-        ck[c] = 16 * g;
-        cbase[c] = r < nrows ? (uint32_t)(r * ldc + 16 * g) : kOOB;
-    }
+    // load slots: X instruction c covers slot p = 256 c + tid, row 32 c + tid / 8, granule
+    // (tid % 8) ^ swz_a(row), which is the same for every c; codes instruction c: row 64 c + tid / 4,
+    // granule (tid % 4) ^ swz_b(row), also the same for every c.  Each instruction of a wave
+    // fills 1 KB of consecutive LDS.
+    const int xr0 = tid >> 3;
+    const int xg = (tid & 7) ^ swz_a(xr0);
+    const int cr0 = tid >> 2;
+    const int cg = (tid & 3) ^ swz_b(cr0);
+    const uint32_t xo0 = (uint32_t)(xr0 * ldx + 8 * xg) * 2u;
+    const uint32_t co0 = (uint32_t)(cr0 * ldc + 16 * cg);
+    const uint32_t xstep = (uint32_t)(64 * ldx);       // 32 rows of X, bytes
+    const uint32_t cstep = (uint32_t)(64 * ldc);       // 64 rows of codes, bytes
     const int nst = (int)((K + kTK - 1) / kTK);
     auto issue = [&](int st) {
         const int k0 = st * kTK;
-        uint32_t xo[4], co[2];
+        uint8_t* la = lds + (st & 1) * (kAS + kBS);
+        uint8_t* lb = la + kAS;
+        const bool xk_ok = k0 + 8 * xg < K;
+        const bool ck_ok = k0 + 16 * cg < K;
+        // a lane past M, N or K reads offset kOOB (mask arithmetic, so that the compiler keeps one
+        // load per slot rather than branching around two)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xo[c] = (xbase[c] != kOOB && k0 + xk[c] < K) ? xbase[c] + (uint32_t)k0 * 2u : kOOB;
+        for (int c = 0; c < kXI; ++c) {
+            const uint32_t bad = 0u - (uint32_t)!(xk_ok && xr0 + 32 * c < mrows);
+            const uint32_t o = ((xo0 + (uint32_t)c * xstep + (uint32_t)k0 * 2u) & ~bad) | (kOOB & bad);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(la + (c * 256 + wave * 64) * 16), 16, o, 0, 0, 0);
+        }
 #pragma unroll
-        for (int c = 0; c < 2; ++c) co[c] = (cbase[c] != kOOB && k0 + ck[c] < K) ? cbase[c] + (uint32_t)k0 : kOOB;
-        uint8_t* base = lds + (st % kStages) * (kAStage + kBStage);
-        stage_loads(xr, cr, base, base + kAStage, wave, xo, co);
+        for (int c = 0; c < 2; ++c) {
+            const uint32_t bad = 0u - (uint32_t)!(ck_ok && cr0 + 64 * c < nrows);
+            const uint32_t o = ((co0 + (uint32_t)c * cstep + (uint32_t)k0) & ~bad) | (kOOB & bad);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_ptr)(lb + (c * 256 + wave * 64) * 16), 16, o, 0, 0, 0);
+        }
     };
 
-    const int wm = (wave >> 1) * 64;
+    const int wm = (wave >> 1) * (32 * kIB);
     const int wn = (wave & 1) * 64;
     const int r32 = lane & 31;
     const int h = lane >> 5;
@@ -292,25 +291,14 @@ __global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restri
         sc[j] = n < N ? half_to_float(scales[n]) : 0.0f;
         sc128[j] = -128.0f * sc[j];                      // exact
     }
-
-    f32x16 acc[2][2];
+    f32x16 acc[kIB][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kIB; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // one 32-wide K block of the stage at la / lb: 8 MFMAs per wavefront
+    // one 32-wide K block of the stage at la / lb: 16 MFMAs per wavefront
     auto block = [&](const uint8_t* la, const uint8_t* lb, int kb) {
-        bf16x8 fa[2][2];                                 // [i][t]
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = wm + 32 * i + r32;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int g = 4 * kb + 2 * h + t;
-                fa[i][t] = *reinterpret_cast<const bf16x8*>(la + (r * 8 + (g ^ swz_a(r))) * 16);
-            }
-        }
         bf16x8 fb[2][2];                                 // [j][t]
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -320,56 +308,78 @@ __global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restri
             codes_to_bf16(q, sc[j], sc128[j], fb[j][0], fb[j][1]);
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < kIB; ++i) {
+            const int r = wm + 32 * i + r32;
+            bf16x8 fa[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int t = 0; t < 2; ++t) {
+                const int g = 4 * kb + 2 * h + t;
+                fa[t] = *reinterpret_cast<const bf16x8*>(la + (r * 8 + (g ^ swz_a(r))) * 16);
+            }
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t], fb[j][t], acc[i][j], 0, 0, 0);
+        }
     };
-    // stage st: wait for its loads (the later stages already issued may stay in flight), then the
-    // barrier after which every wave's loads of st are in LDS and every wave is done reading the
-    // buffer of st - 1, which the next stage's loads then reuse
+    // stage st: wait for its loads, then the barrier after which every wave's loads of st are in
+    // LDS and every wave is done reading the other buffer, which the next stage's loads then fill
     auto enter = [&](int st) {
-        wait_vm(6 * (min(nst, st + kStages - 1) - st - 1));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
-        if (st + kStages - 1 < nst) issue(st + kStages - 1);
+        if (st + 1 < nst) issue(st + 1);
     };
-    auto stage_lds = [&](int st) { return lds + (st % kStages) * (kAStage + kBStage); };
 
-#pragma unroll
-    for (int st = 0; st < kStages - 1; ++st)
-        if (st < nst) issue(st);
+    if (nst > 0) issue(0);
     const int nfull = (int)(K / kTK);                    // stages with both 32-wide blocks in range
     for (int st = 0; st < nfull; ++st) {
         enter(st);
-        const uint8_t* la = stage_lds(st);
-        block(la, la + kAStage, 0);
-        block(la, la + kAStage, 1);
+        const uint8_t* la = lds + (st & 1) * (kAS + kBS);
+        block(la, la + kAS, 0);
+        block(la, la + kAS, 1);
     }
     const int ktail = (int)(K % kTK);                    // 0, 16, 32 or 48
     if (ktail) {
         enter(nfull);
-        const uint8_t* la = stage_lds(nfull);
-        block(la, la + kAStage, 0);
-        if (ktail > 32) block(la, la + kAStage, 1);
+        const uint8_t* la = lds + (nfull & 1) * (kAS + kBS);
+        block(la, la + kAS, 0);
+        if (ktail > 32) block(la, la + kAS, 1);
     }
 
-    // Y is written once and never read here: non-temporal stores.  For register r, lanes 0..31
-    // hold 32 consecutive columns of one row and lanes 32..63 those of the row 4 below.
+    // Y through an LDS transpose, one 32-row block at a time: 16-byte non-temporal stores of 4
+    // consecutive columns (one wavefront instruction covers 4 rows x 256 bytes).  Y is written once
+    // and never read here.  ldy % 4 == 0 and a 16-byte aligned Y are required (host-checked).
+    float* tl = reinterpret_cast<float*>(lds) + wave * (32 * 68);   // rows padded to 68 floats
+    lds_barrier();
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kIB; ++i) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + wn + 32 * j + r32;
-            if (col < N) {
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (row < M) __builtin_nontemporal_store(acc[i][j][r], (GLB float*)y + row * ldy + col);
+            for (int r = 0; r < 16; ++r)
+                tl[(8 * (r >> 2) + 4 * h + (r & 3)) * 68 + 32 * j + r32] = acc[i][j][r];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int c = lane + 64 * q;
+            const int rr = c >> 4, ch = c & 15;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(tl + rr * 68 + 4 * ch);
+            const int64_t row = m0 + wm + 32 * i + rr;
+            const int64_t col = n0 + wn + 4 * ch;
+            if (row < M) {
+                GLB float* py = (GLB float*)y + row * ldy + col;
+                if (col + 4 <= N) {
+                    __builtin_nontemporal_store(v, (GLB f32x4*)py);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < N) __builtin_nontemporal_store(v[e], py + e);
                 }
             }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
 }
 
 }  // namespace
@@ -377,19 +387,22 @@ __global__ void __launch_bounds__(256) pgq_qgemm_kernel(const uint16_t* __restri
 int launch_qgemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
                  const uint16_t* scales, int64_t N, float* y, int64_t ldy, uint32_t flags, void* stream)
 {
-    const uint64_t tiles = (uint64_t)((N + 127) / 128) * (uint64_t)((M + 127) / 128);
-    if (tiles > 0xFFFFFFFFull) return (int)hipErrorInvalidValue;
-    const dim3 grid((unsigned)tiles);
-    // the main kernel: 16-byte loadable X and code rows, K a positive multiple of 16, and a tile's
-    // 128 rows of either operand within a 32-bit buffer range
-    const bool main = (flags & 3u) == 3u && K > 0 && K % 16 == 0 && ldx < ((int64_t)1 << 22) &&
+    // the main kernel: 16-byte loadable X and code rows and 16-byte aligned Y rows (flags bits 0..2),
+    // K a positive multiple of 16, and a tile's rows of either operand within a 31-bit buffer range
+    const bool main = (flags & 7u) == 7u && K > 0 && K % 16 == 0 && ldx < ((int64_t)1 << 21) &&
                       ldc < ((int64_t)1 << 23);
     if (main) {
+        const uint64_t tiles = (uint64_t)((N + kTN - 1) / kTN) * (uint64_t)((M + kTM - 1) / kTM);
+        if (tiles > 0xFFFFFFFFull) return (int)hipErrorInvalidValue;
         void* args[] = {&x, &M, &K, &ldx, &codes, &ldc, &scales, &N, &y, &ldy};
-        return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_kernel), grid, dim3(256), args, stream);
+        return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_kernel), dim3((unsigned)tiles), dim3(256),
+                                 args, stream);
     }
+    const uint64_t tiles = (uint64_t)((N + kBN - 1) / kBN) * (uint64_t)((M + kBM - 1) / kBM);
+    if (tiles > 0xFFFFFFFFull) return (int)hipErrorInvalidValue;
     void* args[] = {&x, &M, &K, &ldx, &codes, &ldc, &scales, &N, &y, &ldy, &flags};
-    return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_generic_kernel), grid, dim3(256), args, stream);
+    return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_generic_kernel), dim3((unsigned)tiles),
+                             dim3(256), args, stream);
 }
 
 }  // namespace pgq
