@@ -215,6 +215,18 @@ pgq_status pgq_export_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_
                             void* arena, float* const* dq_out, void* workspace, size_t workspace_bytes,
                             uint32_t flags, uint32_t* dev_status, void* stream);
 
+/* The same export for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): no workspace argument; the descriptor
+ * table and the whole-tensor select state live in a 4 MiB array of device memory that the library
+ * holds for each GPU it runs on until the process ends.  Nothing is allocated or freed by the call.
+ * Returns PGQ_ERR_WORKSPACE (nothing enqueued) when the call's table needs more than 4 MiB (the
+ * workspace_bytes pgq_export_plan reports is that size).  Every call on one GPU shares its array,
+ * which keeps the last call's table: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  PGQ_TABLE_RESIDENT skips the upload when the
+ * array still holds this call's table (checked by checksum, as for pgq_export_model). */
+pgq_status pgq_export_model_noalloc(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan* plan, void* arena,
+                                    float* const* dq_out, uint32_t flags, uint32_t* dev_status, void* stream);
+
 /* ------------------------------------------------------------------------------------------ */
 /* SQWA: fold snapshot k (1-based) into per-tensor fp32 running means.                         */
 /* Source: "Discriminative TTT + SLOT-24" card (PR #1414), Novel Contributions: average        */

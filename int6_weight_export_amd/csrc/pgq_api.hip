@@ -517,6 +517,60 @@ pgq_status export_desc(const pgq_tensor_in& t, const pgq_tensor_plan& p, uint8_t
     return PGQ_OK;
 }
 
+// ---- the allocation-free export's scratch ------------------------------------------------------
+// pgq_export_model_noalloc keeps its descriptor table (and the whole-tensor select state) in this
+// file-scope array instead of a caller workspace.  Each GPU holds its own copy until the process
+// ends; in host code `scratch` only names the symbol, so its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that address is used.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;         // per device: the address of that device's `scratch`
+
+pgq_status scratch_for_current_device(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_failed(e);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_failed(e);
+        if (!p) return PGQ_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PGQ_OK;
+}
+
+// Descriptors of an export call (shared by both export entry points).
+pgq_status export_descs(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan* plan, void* arena,
+                        float* const* dq_out, std::vector<Desc>& descs)
+{
+    if (!t || !plan) return PGQ_ERR_NULL;
+    if (!arena) return PGQ_ERR_NULL;
+    if (!aligned(arena, 256)) return PGQ_ERR_ALIGN;
+    descs.resize((size_t)n);
+    for (int32_t i = 0; i < n; ++i) {
+        pgq_status st = check_tensor_in(t[i]);
+        if (st != PGQ_OK) return st;
+        st = check_plan_entry(plan[i]);
+        if (st != PGQ_OK) return st;
+        st = export_desc(t[i], plan[i], static_cast<uint8_t*>(arena), descs[i]);
+        if (st != PGQ_OK) return st;
+        if (dq_out && dq_out[i]) {
+            if (!aligned(dq_out[i], 4)) return PGQ_ERR_ALIGN;
+            descs[i].dq = dq_out[i];
+        }
+        set_vec_flag(descs[i]);
+        set_grouping(descs[i], MODE_EXPORT);
+    }
+    return PGQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -713,25 +767,25 @@ pgq_status pgq_export_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor_
 {
     if (n < 0) return PGQ_ERR_SHAPE;
     if (n == 0) return PGQ_OK;
-    if (!t || !plan) return PGQ_ERR_NULL;
-    if (!arena) return PGQ_ERR_NULL;
-    if (!aligned(arena, 256)) return PGQ_ERR_ALIGN;
-    std::vector<Desc> descs((size_t)n);
-    for (int32_t i = 0; i < n; ++i) {
-        pgq_status st = check_tensor_in(t[i]);
-        if (st != PGQ_OK) return st;
-        st = check_plan_entry(plan[i]);
-        if (st != PGQ_OK) return st;
-        st = export_desc(t[i], plan[i], static_cast<uint8_t*>(arena), descs[i]);
-        if (st != PGQ_OK) return st;
-        if (dq_out && dq_out[i]) {
-            if (!aligned(dq_out[i], 4)) return PGQ_ERR_ALIGN;
-            descs[i].dq = dq_out[i];
-        }
-        set_vec_flag(descs[i]);
-        set_grouping(descs[i], MODE_EXPORT);
-    }
+    std::vector<Desc> descs;
+    const pgq_status st = export_descs(t, n, plan, arena, dq_out, descs);
+    if (st != PGQ_OK) return st;
     return run_grouped(MODE_EXPORT, descs, workspace, workspace_bytes, flags, dev_status, 0, 0, stream);
+}
+
+pgq_status pgq_export_model_noalloc(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan* plan, void* arena,
+                                    float* const* dq_out, uint32_t flags, uint32_t* dev_status, void* stream)
+{
+    if (n < 0) return PGQ_ERR_SHAPE;
+    if (n == 0) return PGQ_OK;
+    std::vector<Desc> descs;
+    pgq_status st = export_descs(t, n, plan, arena, dq_out, descs);
+    if (st != PGQ_OK) return st;
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != PGQ_OK) return st;
+    // a table larger than the array is refused (PGQ_ERR_WORKSPACE) before anything is enqueued
+    return run_grouped(MODE_EXPORT, descs, ws, kScratchBytes, flags, dev_status, 0, 0, stream);
 }
 
 pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_tensor_plan* plan,

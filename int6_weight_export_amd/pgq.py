@@ -91,6 +91,8 @@ SIGNATURES = {
                                ctypes.POINTER(pgq_tensor_plan), ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "pgq_export_model": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan), _P,
                                 ctypes.POINTER(_P), _P, _SZ, _U32, _P, _P]),
+    "pgq_export_model_noalloc": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan), _P,
+                                        ctypes.POINTER(_P), _U32, _P, _P]),
     "pgq_sqwa_accumulate": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan),
                                    ctypes.POINTER(_P), _I32, _P, _SZ, _U32, _P, _P]),
     "pgq_dequant_codes": (_I32, [_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
@@ -153,6 +155,10 @@ def pgq_export_plan(t, n, pol, plan, arena_bytes, workspace_bytes):
 def pgq_export_model(t, n, plan, arena, dq_out, workspace, workspace_bytes, flags, dev_status, stream):
     return _lib.pgq_export_model(t, n, plan, arena, dq_out, workspace, workspace_bytes, flags, dev_status,
                                  stream)
+
+
+def pgq_export_model_noalloc(t, n, plan, arena, dq_out, flags, dev_status, stream):
+    return _lib.pgq_export_model_noalloc(t, n, plan, arena, dq_out, flags, dev_status, stream)
 
 
 def pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flags, dev_status, stream):
