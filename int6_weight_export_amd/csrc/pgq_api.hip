@@ -22,50 +22,13 @@ using namespace pgq;
 
 namespace {
 
-int env_int(const char* name, int dflt, int lo, int hi)
-{
-    const char* v = getenv(name);
-    if (!v || !*v) return dflt;
-    int x = atoi(v);
-    return std::min(std::max(x, lo), hi);
-}
-
-// Row groups per wavefront in one tile (a tile is kWaves * rgroup * groups rows of a tensor).
-int groups_per_wave()
-{
-    static const int v = env_int("PGQ_GROUPS_PER_WAVE", 1, 1, 64);
-    return v;
-}
-
-// Row groups per wavefront in a tile of a tensor with AWQ multipliers: the workgroup computes
-// the multipliers (and their reciprocals) once per tile, so longer tiles amortise that.
-int awq_groups_per_wave()
-{
-    static const int v = env_int("PGQ_AWQ_GROUPS_PER_WAVE", 2, 1, 64);
-    return v;
-}
-
-// Export tiles per workgroup of a whole-tensor select pass.
-int sel_group()
-{
-    static const int v = env_int("PGQ_SEL_GROUP", 3, 1, 64);   // measured best of 1, 2, 3, 4, 8
-    return v;
-}
-
-// Upper bound on the rows a wavefront processes together.
-int max_rgroup()
-{
-    static const int v = env_int("PGQ_MAX_RGROUP", 0, 0, 8);   // 0: per-mode default
-    return v;
-}
-
-// Workgroups per compute unit when the grid is made persistent (0: one workgroup per tile,
-// which lets the hardware dispatcher balance the load; measured faster on MI355X).
-int wg_per_cu_override()
-{
-    static const int v = env_int("PGQ_WG_PER_CU", 0, 0, 64);
-    return v;
-}
+// Launch geometry, fixed from measurements on MI355X.
+constexpr int kGroupsPerWave = 1;       // row groups per wavefront in one tile (a tile is
+                                        // kWaves * rgroup * groups rows of a tensor)
+constexpr int kAwqGroupsPerWave = 2;    // the same for tensors with AWQ multipliers: the workgroup
+                                        // builds the multiplier table once per tile
+constexpr int kSelGroup = 3;            // export tiles per workgroup of a radix select pass
+constexpr uint32_t kCandMaxRank = 256;  // candidate select up to this rank from the top
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -160,63 +123,76 @@ Desc blank_desc()
     return d;
 }
 
-struct LimitCache {
-    std::mutex mu;
-    // [device][mode][variant] -> resident blocks per CU; n_cu per device
-    std::vector<std::vector<int>> per_cu;
-    std::vector<int> n_cu;
-};
-LimitCache g_limits;
-
-uint32_t grid_for(int mode, uint32_t need, bool table, uint32_t n_tiles)
-{
-    if (wg_per_cu_override() == 0) return std::max<uint32_t>(1, n_tiles);
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    int per_cu = 0, ncu = 0;
-    {
-        std::lock_guard<std::mutex> lk(g_limits.mu);
-        if ((int)g_limits.per_cu.size() <= dev) {
-            g_limits.per_cu.resize(dev + 1, std::vector<int>(2 * kModes * 128, -1));
-            g_limits.n_cu.resize(dev + 1, -1);
-        }
-        int& slot = g_limits.per_cu[dev][(table ? kModes * 128 : 0) + mode * 128 + variant_of(mode, need)];
-        if (slot < 0 || g_limits.n_cu[dev] < 0) {
-            int pc = 0, nc = 0;
-            if (max_resident_blocks(mode, need, table, &pc, &nc) != 0 || pc <= 0 || nc <= 0) { pc = 4; nc = 256; }
-            slot = pc;
-            g_limits.n_cu[dev] = nc;
-        }
-        per_cu = slot;
-        ncu = g_limits.n_cu[dev];
-    }
-    per_cu = std::min(per_cu, wg_per_cu_override());
-    const uint64_t g = (uint64_t)per_cu * (uint64_t)ncu;
-    return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(g, n_tiles));
-}
+// One workgroup per tile: the hardware dispatcher balances the load (a persistent grid striding
+// over the tiles measured ~10% slower).
+uint32_t grid_for(uint32_t n_tiles) { return std::max<uint32_t>(1, n_tiles); }
 
 // Workspace layout of a grouped call: header | descriptors | first tile per tensor | tensor per
-// tile | (per-tensor scales) first tile per tensor and tensor per tile of the select passes |
-// one TState per tensor.  The last three parts are uploaded only when a call needs them.
+// tile | (per-tensor scales) first tile per tensor and tensor per tile of the radix select passes
+// and of the candidate pass | one TState per tensor | candidate keys.  The parts after the main
+// table are uploaded only when a call selects (the TStates start at zero); the candidate region
+// is never uploaded.
 struct TableLayout {
-    size_t desc_off, start_off, tdesc_off, start2_off, tdesc2_off, state_off, end_main, end;
+    size_t desc_off, start_off, tdesc_off, end_main, start2_off, tdesc2_off, start3_off, tdesc3_off, state_off,
+        state_end, cand_off, end;
 };
 
-TableLayout table_layout(size_t n_desc, uint64_t n_tiles)
+TableLayout table_layout(size_t n_desc, uint64_t n_tiles, uint64_t cand_words)
 {
     TableLayout L;
+    const int64_t starts = align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 64);
+    const int64_t tiles = align_up((int64_t)(n_tiles * sizeof(uint32_t)), 64);
     L.desc_off = sizeof(TableHeader);
     L.start_off = L.desc_off + align_up((int64_t)(n_desc * sizeof(Desc)), 64);
-    L.tdesc_off = L.start_off + align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 64);
+    L.tdesc_off = L.start_off + starts;
     L.end_main = L.tdesc_off + align_up((int64_t)(n_tiles * sizeof(uint32_t)), 8);
     L.start2_off = align_up((int64_t)L.end_main, 64);
-    L.tdesc2_off = L.start2_off + align_up((int64_t)((n_desc + 1) * sizeof(uint32_t)), 64);
-    L.state_off = L.tdesc2_off + align_up((int64_t)(n_tiles * sizeof(uint32_t)), 64);
-    L.end = L.state_off + n_desc * sizeof(TState);
+    L.tdesc2_off = L.start2_off + starts;
+    L.start3_off = L.tdesc2_off + tiles;
+    L.tdesc3_off = L.start3_off + starts;
+    L.state_off = L.tdesc3_off + tiles;
+    L.state_end = L.state_off + n_desc * sizeof(TState);
+    L.cand_off = align_up((int64_t)L.state_end, 256);
+    L.end = L.cand_off + cand_words * sizeof(uint32_t);
     return L;
 }
 
-size_t table_bytes(size_t n_desc, uint64_t n_tiles) { return table_layout(n_desc, n_tiles).end; }
+size_t table_bytes(size_t n_desc, uint64_t n_tiles, uint64_t cand_words = 0)
+{
+    return table_layout(n_desc, n_tiles, cand_words).end;
+}
+
+// Candidate select geometry: a lane of a candidate tile holds kCandKeys keys, and one row gives
+// it ceil(cols / (64 vec)) slots of vec elements; rows per wavefront, 0 when a row does not fit.
+int cand_rows_per_wave(int64_t cols, int vec)
+{
+    const int64_t per_row = ((cols / vec + 63) / 64) * vec;
+    return per_row > 32 ? 0 : (int)(32 / per_row);
+}
+
+// Keys a candidate tile may append: twice the rank plus slack (a tile appends every key at or
+// above its bound, about the rank for independent values; beyond this it appends its exact
+// rank_top largest instead).
+uint32_t cand_cap(int64_t rank) { return (uint32_t)((2 * rank + 32 + 3) & ~(int64_t)3); }
+
+// Words of one tensor's candidate region: ccap slots per tile, then one count per tile.
+uint64_t cand_region_words(uint64_t tiles, uint32_t ccap) { return (uint64_t)align_up((int64_t)(tiles * ccap + tiles), 16); }
+
+// Candidate words a per-tensor tensor needs, whichever load path (vector or element-wise) its
+// export takes; 0 when it uses the radix select.
+uint64_t cand_words_bound(int64_t rows, int64_t cols, int32_t dtype, int64_t rank)
+{
+    if (rank > (int64_t)kCandMaxRank || rows <= 0 || cols <= 0) return 0;
+    const int vec = dtype == PGQ_F32 ? 4 : 8;
+    int rpw = cand_rows_per_wave(cols, 1);
+    if (cols % vec == 0) {
+        const int rv = cand_rows_per_wave(cols, vec);
+        rpw = std::min(rpw, rv);
+    }
+    if (rpw <= 0) return 0;
+    const int64_t tiles = (rows + (int64_t)kWaves * rpw - 1) / ((int64_t)kWaves * rpw);
+    return cand_region_words((uint64_t)tiles, cand_cap(rank));
+}
 
 // Rows a wavefront loads together: as many as the register tile holds (a power of two), and
 // the exact chunk count per lane of a row on the vector path.
@@ -236,7 +212,7 @@ void set_grouping(Desc& d, int mode)
             while (p2 < nch) p2 <<= 1;
             // measured: STE rows (bf16, two input streams) gain from two rows per wavefront,
             // export and SQWA rows from one
-            const int cap = max_rgroup() > 0 ? max_rgroup() : (mode == MODE_FQ ? 2 : 1);
+            const int cap = mode == MODE_FQ ? 2 : 1;
             R = std::min(std::min(ncht / p2, 8), cap);
             int r2 = 1;
             while (r2 * 2 <= R) r2 *= 2;
@@ -245,7 +221,7 @@ void set_grouping(Desc& d, int mode)
     }
     d.rgroup = R;
     const bool awq_tile = d.awq_s && d.kind != KIND_F16 && mode != MODE_FQ && mode != MODE_FQ_BWD;
-    d.tile_rows = kWaves * R * std::max(groups_per_wave(), awq_tile ? awq_groups_per_wave() : 1);
+    d.tile_rows = kWaves * R * std::max(kGroupsPerWave, awq_tile ? kAwqGroupsPerWave : 1);
 }
 
 // Upper bound on the tiles of a tensor (group size 1), for sizing workspaces before the
@@ -253,7 +229,7 @@ void set_grouping(Desc& d, int mode)
 uint64_t max_tiles_for(int64_t rows, int64_t cols)
 {
     if (rows <= 0 || cols <= 0) return 0;
-    const int64_t tr = (int64_t)kWaves * groups_per_wave();
+    const int64_t tr = (int64_t)kWaves * kGroupsPerWave;
     return (uint64_t)((rows + tr - 1) / tr);
 }
 
@@ -296,41 +272,62 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
     }
     start[n] = (uint32_t)total;
     if (total == 0) return PGQ_OK;
-    const TableLayout L = table_layout(n, total);
-    // per-tensor scales: the select passes run over the tiles of those tensors only, sel_group()
-    // export tiles per select workgroup
-    const uint64_t kSelGroup = (uint64_t)sel_group();
-    std::vector<uint32_t> start2(n + 1, 0);
-    uint64_t total2 = 0;
+    // per-tensor scales (only an export selects; a decode's DF_TENSOR just means "scale 0 for
+    // every row"): the clip of a tensor with rank_top <= kCandMaxRank and rows that fit a
+    // candidate tile comes from the one-read candidate pass, any other from the radix passes
+    // (kSelGroup export tiles per workgroup)
+    const TableLayout L0 = table_layout(n, total, 0);
+    std::vector<uint32_t> start2(n + 1, 0), start3(n + 1, 0);
+    uint64_t total2 = 0, total3 = 0, cand_words = 0;
     int passes = 0;
-    // (only an export selects; a decode's DF_TENSOR just means "scale 0 for every row")
     const bool selects = mode == MODE_EXPORT || mode == MODE_EXPORT6;
     for (size_t i = 0; i < n; ++i) {
         start2[i] = (uint32_t)total2;
-        if (selects && (descs[i].flags & DF_TENSOR)) {
-            if (!descs[i].w && tiles_for(descs[i]) > 0) return PGQ_ERR_NULL;   // the select reads the weights
-            total2 += (tiles_for(descs[i]) + kSelGroup - 1) / kSelGroup;
-            passes = std::max(passes, descs[i].rank_top > 1 ? 4 : 1);
-            descs[i].tstate = reinterpret_cast<TState*>(static_cast<uint8_t*>(ws) + L.state_off) + i;
+        start3[i] = (uint32_t)total3;
+        Desc& d = descs[i];
+        if (selects && (d.flags & DF_TENSOR) && d.rows > 0 && d.cols > 0) {
+            if (!d.w) return PGQ_ERR_NULL;                          // the select reads the weights
+            d.tstate = reinterpret_cast<TState*>(static_cast<uint8_t*>(ws) + L0.state_off) + i;
+            const bool vec = (d.flags & DF_VEC) != 0;
+            const int rpw = cand_rows_per_wave(d.cols, vec ? (d.in_dtype == IN_F32 ? 4 : 8) : 1);
+            if (d.rank_top <= (int64_t)kCandMaxRank && rpw > 0) {
+                d.flags |= DF_CAND;
+                d.crows = kWaves * rpw;
+                d.ccap = (int32_t)cand_cap(d.rank_top);
+                const uint64_t ct = (uint64_t)((d.rows + d.crows - 1) / d.crows);
+                d.cand = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + L0.cand_off) + cand_words;
+                cand_words += cand_region_words(ct, (uint32_t)d.ccap);
+                total3 += ct;
+            } else {
+                total2 += (tiles_for(d) + kSelGroup - 1) / kSelGroup;
+                passes = std::max(passes, d.rank_top > 1 ? 4 : 1);
+            }
         }
     }
     start2[n] = (uint32_t)total2;
-    const size_t need = passes ? L.end : L.end_main;
+    start3[n] = (uint32_t)total3;
+    const bool select = passes > 0 || total3 > 0;
+    const TableLayout L = table_layout(n, total, cand_words);
+    const size_t need = select ? L.end : L.end_main;            // bytes the call uses
+    const size_t upload = select ? L.state_end : L.end_main;    // bytes the host writes
     if (!ws) return PGQ_ERR_WORKSPACE;
     if (ws_bytes < need) return PGQ_ERR_WORKSPACE;
     if (!aligned(ws, 64)) return PGQ_ERR_ALIGN;
 
-    // The checksum covers the descriptors and both tile prefixes (the per-tile tensor indices
-    // are functions of them), so a call on a resident table hashes ~n * 170 bytes and builds
-    // nothing else.
+    // The checksum covers the descriptors and the tile prefixes (the per-tile tensor indices are
+    // functions of them), so a call on a resident table hashes ~n * 180 bytes and builds nothing
+    // else.
     uint64_t h = table_hash(descs.data(), n * sizeof(Desc), 0x243F6A8885A308D3ull ^ (uint64_t)mode);
     h = table_hash(start.data(), (n + 1) * sizeof(uint32_t), h);
     h = table_hash(&total, 8, h);
-    if (passes) h = table_hash(start2.data(), (n + 1) * sizeof(uint32_t), h);
+    if (select) {
+        h = table_hash(start2.data(), (n + 1) * sizeof(uint32_t), h);
+        h = table_hash(start3.data(), (n + 1) * sizeof(uint32_t), h);
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!(flags & PGQ_TABLE_RESIDENT)) {
-        std::vector<uint64_t> buf8((need + 7) / 8, 0);
+        std::vector<uint64_t> buf8((upload + 7) / 8, 0);
         uint8_t* buf = reinterpret_cast<uint8_t*>(buf8.data());
         TableHeader* hdr = reinterpret_cast<TableHeader*>(buf);
         memcpy(buf + L.desc_off, descs.data(), n * sizeof(Desc));
@@ -338,18 +335,22 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
         uint32_t* tdesc = reinterpret_cast<uint32_t*>(buf + L.tdesc_off);
         for (size_t i = 0; i < n; ++i)
             for (uint32_t t = start[i]; t < start[i + 1]; ++t) tdesc[t] = (uint32_t)i;
-        if (passes) {
+        if (select) {                                      // the TStates start at zero
             memcpy(buf + L.start2_off, start2.data(), (n + 1) * sizeof(uint32_t));
+            memcpy(buf + L.start3_off, start3.data(), (n + 1) * sizeof(uint32_t));
             uint32_t* tdesc2 = reinterpret_cast<uint32_t*>(buf + L.tdesc2_off);
-            for (size_t i = 0; i < n; ++i)                 // the TStates start at zero
+            uint32_t* tdesc3 = reinterpret_cast<uint32_t*>(buf + L.tdesc3_off);
+            for (size_t i = 0; i < n; ++i) {
                 for (uint32_t t = start2[i]; t < start2[i + 1]; ++t) tdesc2[t] = (uint32_t)i;
+                for (uint32_t t = start3[i]; t < start3[i + 1]; ++t) tdesc3[t] = (uint32_t)i;
+            }
         }
         hdr->magic = kTableMagic;
         hdr->checksum = h;
         hdr->n_desc = (uint32_t)n;
         hdr->n_tiles = (uint32_t)total;
         // A pageable source is staged by the runtime before this call returns.
-        const hipError_t e = hipMemcpyAsync(ws, buf, need, hipMemcpyHostToDevice, s);
+        const hipError_t e = hipMemcpyAsync(ws, buf, upload, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return hip_failed(e);
     }
     const uint8_t* base = static_cast<const uint8_t*>(ws);
@@ -366,24 +367,35 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
     ka.avg_c = avg_c;
     void *ev_start = nullptr, *ev_stop = nullptr;
     take_timing_events(&ev_start, &ev_stop);
-    // the whole-tensor clip select: one launch per digit and the final pick, then the main launch
-    if (passes) {
-        uint32_t feats2 = 0;
+    // the whole-tensor clip select -- the candidate pass and / or one launch per radix digit --
+    // and the final pick, then the main launch
+    if (select) {
+        uint32_t fc = 0, fr = 0;
         for (const Desc& d : descs)
-            if (d.flags & DF_TENSOR) feats2 |= features_avg(d);
+            if (d.flags & DF_TENSOR) ((d.flags & DF_CAND) ? fc : fr) |= features_avg(d);
+        if (total3) {
+            KArgs k3 = ka;
+            k3.tile_start = reinterpret_cast<const uint32_t*>(base + L.start3_off);
+            k3.tile_desc = reinterpret_cast<const uint32_t*>(base + L.tdesc3_off);
+            k3.n_tiles = (uint32_t)total3;
+            set_timing_events(ev_start, nullptr);
+            ev_start = nullptr;
+            if (const int e = launch(MODE_TCAND, fc, k3, nullptr, grid_for(k3.n_tiles), stream))
+                return hip_failed((hipError_t)e);
+        }
         KArgs k2 = ka;
         k2.tile_start = reinterpret_cast<const uint32_t*>(base + L.start2_off);
         k2.tile_desc = reinterpret_cast<const uint32_t*>(base + L.tdesc2_off);
         k2.n_tiles = (uint32_t)total2;
-        k2.tsel_group = (int32_t)kSelGroup;
-        const uint32_t grid2 = grid_for(MODE_TSEL, feats2, true, k2.n_tiles);
+        k2.tsel_group = kSelGroup;
         for (int p = 0; p < passes; ++p) {
             k2.tsel_pass = p;
-            set_timing_events(p == 0 ? ev_start : nullptr, nullptr);
-            if (const int e = launch(MODE_TSEL, feats2, k2, nullptr, grid2, stream)) return hip_failed((hipError_t)e);
+            set_timing_events(ev_start, nullptr);
+            ev_start = nullptr;
+            if (const int e = launch(MODE_TSEL, fr, k2, nullptr, grid_for(k2.n_tiles), stream))
+                return hip_failed((hipError_t)e);
         }
         if (const int e = launch_tensor_pick(k2, (uint32_t)n, stream)) return hip_failed((hipError_t)e);
-        ev_start = nullptr;
     }
     ka.tile_start = reinterpret_cast<const uint32_t*>(base + L.start_off);
     ka.tile_desc = reinterpret_cast<const uint32_t*>(base + L.tdesc_off);
@@ -391,7 +403,7 @@ pgq_status run_grouped(int mode, const std::vector<Desc>& descs_in, void* ws, si
     const bool averaging = mode == MODE_EMA || mode == MODE_SWA;
     uint32_t feats = 0;
     for (const Desc& d : descs) feats |= averaging ? features_avg(d) : features_of(d);
-    const uint32_t grid = grid_for(mode, feats, true, ka.n_tiles);
+    const uint32_t grid = grid_for(ka.n_tiles);
     set_timing_events(ev_start, ev_stop);
     if (const int e = launch(mode, feats, ka, nullptr, grid, stream)) return hip_failed((hipError_t)e);
     if (const hipError_t e = hipGetLastError()) return hip_failed(e);
@@ -410,7 +422,7 @@ pgq_status run_single(int mode, const Desc& d, uint32_t* dev_status, int sqwa_k,
     ka.sqwa_k = sqwa_k;
     ka.fq_mode = fq_mode;
     const uint32_t need = features_of(d);
-    const uint32_t grid = grid_for(mode, need, false, ka.n_tiles);
+    const uint32_t grid = grid_for(ka.n_tiles);
     if (const int e = launch(mode, need, ka, &d, grid, stream)) return hip_failed((hipError_t)e);
     if (const hipError_t e = hipGetLastError()) return hip_failed(e);
     return PGQ_OK;
@@ -723,7 +735,7 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
     if (pol->per_tensor != 0 && pol->per_tensor != 1) return PGQ_ERR_PARAM;
     if (pol->pack6 != 0 && pol->pack6 != 1) return PGQ_ERR_PARAM;
     int64_t off = 0;
-    uint64_t nt = 0;
+    uint64_t nt = 0, cand = 0;
     for (int32_t i = 0; i < n; ++i) {
         const pgq_tensor_in& x = t[i];
         nt += max_tiles_for(x.rows, x.cols);
@@ -745,6 +757,7 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
             p.per_tensor = pol->per_tensor ? 1 : 0;
             if (p.per_tensor && p.has_awq) return PGQ_ERR_PARAM;
             if (p.per_tensor && numel >= (int64_t(1) << 32)) return PGQ_ERR_SHAPE;
+            if (p.per_tensor) cand += cand_words_bound(x.rows, x.cols, x.dtype, rank_top(numel, p.qp.pct_num, p.qp.pct_den));
             p.packed = (pol->pack6 && p.kind == 6) ? 1 : 0;
             p.codes_off = off;
             off = align_up(off + (p.packed ? x.rows * (3 * ((x.cols + 3) / 4)) : numel), 256);
@@ -757,7 +770,7 @@ pgq_status pgq_export_plan(const pgq_tensor_in* t, int32_t n, const pgq_policy* 
         }
     }
     *arena_bytes = (size_t)std::max<int64_t>(off, 256);
-    *workspace_bytes = table_bytes((size_t)n, nt);
+    *workspace_bytes = table_bytes((size_t)n, nt, cand);
     return PGQ_OK;
 }
 

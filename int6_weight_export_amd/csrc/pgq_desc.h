@@ -52,19 +52,18 @@ enum : uint32_t {
 
 // State of one tensor's whole-tensor clip select, in the caller's workspace.
 // Candidate select (DF_CAND, one read of the tensor): every workgroup of the MODE_TCAND launch
-// appends the keys of its rows that can still be the clip to the tensor's candidate array
-// (Desc::cand), taking its place with an atomic add on ncand; the pick ranks them.
+// stores the keys of its rows that can still be the clip in its own slots of the tensor's
+// candidate array (Desc::cand: ccap keys per tile, then one count per tile); the pick ranks them.
 // Radix select: pass p adds every workgroup's LDS histogram of key digit p (bits 30..23,
 // 22..15, 14..7, 6..0 of |x|, among the keys matching the digits already chosen) into hist[p];
 // the digits chosen so far are re-derived from hist[0 .. p-1] by whoever needs them.
-// The final pick stores the selected key and zeroes hist / kmax / ncand, so consecutive calls
-// need no reset.
+// The final pick stores the selected key and zeroes hist / kmax, so consecutive calls need no
+// reset.
 struct alignas(64) TState {
     uint32_t hist[4][256];
     uint32_t kmax;        // absmax select: running maximum key
     uint32_t key;         // the selected |x| bit pattern, read by the quantize pass
-    uint32_t ncand;       // candidate select: keys appended so far
-    uint32_t pad[13];
+    uint32_t pad[14];
 };
 
 struct alignas(16) Desc {
@@ -90,9 +89,9 @@ struct alignas(16) Desc {
     int32_t rgroup;           // rows a wave processes together (1, 2, 4 or 8)
     int32_t tile_rows;        // rows per tile: kWaves * rgroup * groups per wave
     int32_t nch;              // vector path: ceil(chunks / 64) per row, 0 when the row streams
-    uint32_t* cand;           // DF_CAND: candidate keys (workspace), ctiles * ccap entries
+    uint32_t* cand;           // DF_CAND: candidate keys (workspace): ccap per tile, then a count per tile
     int32_t crows;            // DF_CAND: rows per candidate tile (kWaves * rows per wave)
-    int32_t ccap;             // DF_CAND: most keys a candidate tile appends
+    int32_t ccap;             // DF_CAND: most keys a candidate tile stores (a multiple of 4)
 };
 
 struct alignas(64) TableHeader {
@@ -123,11 +122,10 @@ struct KArgs {
 
 // Host-side launcher implemented next to the kernels.
 // need: the F_* features of the launch.  variant_of() names the instantiation used (its
-// feature set); launch() and max_resident_blocks() take the same `need`.
+// feature set); launch() takes the same `need`.
 // single: the descriptor of a single-matrix launch, or null for a grouped (table) launch.
 uint32_t variant_of(int mode, uint32_t need);
 int launch(int mode, uint32_t need, const KArgs& ka, const Desc* single, uint32_t grid, void* stream);
-int max_resident_blocks(int mode, uint32_t need, bool table, int* per_cu, int* n_cu);
 // The next launch on this host thread records these hipEvent_t at kernel start / end (either
 // may be null); take_timing_events() hands back and clears a pending pair.
 void set_timing_events(void* start, void* stop);

@@ -123,27 +123,32 @@ __device__ __forceinline__ T ldnt(const GLB T* p) { return __builtin_nontemporal
 template <class T>
 __device__ __forceinline__ void stnt(GLB T* p, T v) { __builtin_nontemporal_store(v, p); }
 
-// VEC consecutive elements starting at element e of a row
-template <int IN, int VEC>
+// a load that may leave its line in the caches (data read again soon)
+template <class T>
+__device__ __forceinline__ T ldkeep(const GLB T* p) { return *p; }
+
+// VEC consecutive elements starting at element e of a row (NT: non-temporal loads)
+template <int IN, int VEC, bool NT = true>
 __device__ __forceinline__ void load_x(const GLB void* row, uint32_t e, float (&x)[VEC])
 {
+    auto ld = [](auto p) { if constexpr (NT) return ldnt(p); else return ldkeep(p); };
     if constexpr (IN == IN_F32) {
         if constexpr (VEC == 4) {
-            const f32x4 v = ldnt(at<f32x4>(row, e * 4u));
+            const f32x4 v = ld(at<f32x4>(row, e * 4u));
             x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
         } else {
             static_assert(VEC == 1, "fp32 path uses VEC 4 or 1");
-            x[0] = ldnt(at<float>(row, e * 4u));
+            x[0] = ld(at<float>(row, e * 4u));
         }
     } else {
         if constexpr (VEC == 8) {
-            const u32x4 v = ldnt(at<u32x4>(row, e * 2u));
+            const u32x4 v = ld(at<u32x4>(row, e * 2u));
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) { x[2 * i] = bitsf(w[i] << 16); x[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u); }
         } else {
             static_assert(VEC == 1, "bf16 path uses VEC 8 or 1");
-            x[0] = bitsf((uint32_t)ldnt(at<uint16_t>(row, e * 2u)) << 16);
+            x[0] = bitsf((uint32_t)ld(at<uint16_t>(row, e * 2u)) << 16);
         }
     }
 }
@@ -1276,12 +1281,216 @@ __device__ __forceinline__ void tile_tensor_select(const Desc& d, int64_t row0, 
     }
 }
 
+// ---- whole-tensor clip select in one read: candidate keys ------------------------------------
+// The clip of a DF_CAND tensor is the R-th largest key (R = rank_top <= kCandMaxRank) over the
+// whole tensor.  A workgroup holds the keys of its tile (crows rows) in registers and stores in
+// its own slots of the tensor's candidate array (ccap keys per tile, then one count per tile)
+// every key that can still be among the R largest of the tensor: those at or above t0, a lower
+// bound on the R-th largest of the workgroup's 256 lane maxima -- R lane maxima are R distinct
+// keys >= t0, so the tile's R largest keys are all >= t0, and the tensor's R largest keys, each
+// among the R largest of its own tile, are all kept.  When more than ccap keys tie at or above
+// t0, the tile stores its exact R largest keys instead (those above its R-th largest key t, then
+// copies of t), found by a radix select over the registers.  pgq_tensor_pick_kernel then finds
+// the R-th largest candidate, which is the tensor's R-th largest key.
+constexpr int kCandKeys = 32;          // keys a lane holds (the host sizes tiles to fit)
+
+// exclusive prefix of v over the lanes below this one (all lanes active), and the wave total
+__device__ __forceinline__ uint32_t wave_prefix(uint32_t v, int lane, uint32_t& total)
+{
+    uint32_t inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t u = (uint32_t)__shfl_up((int)inc, off, 64);
+        if (lane >= off) inc += u;
+    }
+    total = (uint32_t)__shfl((int)inc, 63, 64);
+    return inc - v;
+}
+
+// A lower bound t on the R-th largest of the values the workgroup's threads hold (0 = none), at
+// most one bin below it: bins of 2^16 bit-pattern steps under the largest value M (1/128 of a
+// binade for positive floats), counted in an LDS histogram; t is the smallest value of the first
+// bin, from the top, where the running count reaches R, so at least R values are >= t.  1 when
+// fewer than R values are held or the count reaches R only in the last (clamped) bin.  Whole
+// workgroup of NW wavefronts, uniform result; wl: 257 + 2 NW words of LDS (wl[0..255] is the
+// histogram).
+template <int NW>
+__device__ __forceinline__ uint32_t wg_lower_bound(uint32_t v, uint32_t R, int wave, int lane, uint32_t* wl)
+{
+    const int tid = (int)threadIdx.x;
+    if (tid < 256) wl[tid] = 0;
+    const uint32_t wmax = wave_max(v);
+    const uint32_t wcnt = (uint32_t)__builtin_popcountll(__ballot(v != 0));
+    if (lane == 0) { wl[256 + wave] = wmax; wl[256 + NW + wave] = wcnt; }
+    __syncthreads();
+    uint32_t M = 0, nz = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { M = max(M, wl[256 + w]); nz += wl[256 + NW + w]; }
+    if (nz < R) return 1u;                           // uniform
+    if (v != 0) atomicAdd(&wl[min(255u, (M - v) >> 16)], 1u);
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t h[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) h[b] = wl[4 * lane + b];
+        const uint32_t sum4 = h[0] + h[1] + h[2] + h[3];
+        uint32_t inc = sum4;                         // running count over bins <= 4 lane + 3
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t u = (uint32_t)__shfl_up((int)inc, off, 64);
+            if (lane >= off) inc += u;
+        }
+        uint32_t run = inc - sum4;
+        int found = -1;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (found < 0 && run < R && run + h[b] >= R) found = 4 * lane + b;
+            run += h[b];
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        const int bin = bal ? __shfl(found, __ffsll((unsigned long long)bal) - 1, 64) : 255;
+        const uint32_t edge = (uint32_t)(bin + 1) << 16;
+        if (lane == 0) wl[256 + 2 * NW] = (bin < 255 && M > edge) ? M - edge + 1u : 1u;
+    }
+    __syncthreads();
+    return wl[256 + 2 * NW];
+}
+
+template <int IN, int VEC>
+__device__ __forceinline__ void tile_tensor_cand(const Desc& d, int64_t row0, int wave, int lane, uint32_t* wl,
+                                                 uint32_t& st)
+{
+    const uint32_t tile = (uint32_t)(row0 / d.crows);             // this tile's slots
+    constexpr int NS = kCandKeys / VEC;              // 16-byte (or element) slots per lane
+    const int tid = (int)threadIdx.x;
+    const int nchunk = (int)(d.cols / VEC);
+    const int nch = (nchunk + 63) >> 6;              // slots of a row per lane
+    const int rpw = d.crows / kWaves;                // rows per wave: rpw * nch <= NS (host)
+    const size_t esz = IN == IN_F32 ? 4 : 2;
+    const int64_t rfirst = row0 + (int64_t)wave * rpw;
+    uint32_t key[kCandKeys];
+    uint32_t okm = 0;                                // bit s * VEC + v: key held
+    {
+        int r = 0, i = 0;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int64_t row = rfirst + r;
+            const int c = 64 * i + lane;
+            const bool ok = r < rpw && row < d.rows && c < nchunk;
+            float x[VEC];
+            if (ok) {
+                const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
+                load_x<IN, VEC, false>(wrow, (uint32_t)c * VEC, x);      // the export pass reads them next
+            } else {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) x[v] = 0.0f;
+            }
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) key[s * VEC + v] = fbits(x[v]) & 0x7FFFFFFFu;
+            if (ok) okm |= ((VEC == 32 ? 0u : (1u << VEC)) - 1u) << (s * VEC);
+            if (++i == nch) { i = 0; ++r; }
+        }
+    }
+    // lane maximum, +1 so that 0 means "no key"
+    uint32_t lm = 0, bad = 0;
+#pragma unroll
+    for (int k = 0; k < kCandKeys; ++k)
+        if ((okm >> k) & 1u) {
+            lm = max(lm, key[k] + 1u);
+            bad |= key[k] >= 0x7F800000u ? 1u : 0u;
+        }
+    if (bad) st |= PGQ_DEV_NONFINITE;
+    const uint32_t R = (uint32_t)d.rank_top;
+    const uint32_t t0 = wg_lower_bound<kWaves>(lm, R, wave, lane, wl);   // <= the R-th largest lane maximum
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kCandKeys; ++k) c += (((okm >> k) & 1u) && key[k] + 1u >= t0) ? 1u : 0u;
+    uint32_t wtot;
+    const uint32_t lpre = wave_prefix(c, lane, wtot);
+    if (lane == 0) wl[268 + wave] = wtot;
+    __syncthreads();
+    const uint32_t C = wl[268] + wl[269] + wl[270] + wl[271];
+    const uint32_t ntiles = (uint32_t)((d.rows + d.crows - 1) / d.crows);
+    GLB uint32_t* cand = gp(d.cand) + (size_t)tile * (uint32_t)d.ccap;
+    GLB uint32_t* count = gp(d.cand) + (size_t)ntiles * (uint32_t)d.ccap + tile;
+    uint32_t woff = 0;
+    for (int w = 0; w < wave; ++w) woff += wl[268 + w];
+    if (C <= (uint32_t)d.ccap) {
+        uint32_t pos = woff + lpre;
+#pragma unroll
+        for (int k = 0; k < kCandKeys; ++k)
+            if (((okm >> k) & 1u) && key[k] + 1u >= t0) cand[pos++] = key[k];
+        if (tid == 0) *count = C;
+        return;
+    }
+    // exact R largest keys of the tile: radix select over the registers (digits of bits 30..23,
+    // 22..15, 14..7, 6..0), one 256-bin histogram for the workgroup
+    uint32_t* hist = wl + 512;
+    uint32_t prefix = 0, pmask = 0, rem = R;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
+        hist[tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kCandKeys; ++k)
+            if (((okm >> k) & 1u) && (key[k] & pmask) == prefix) atomicAdd(&hist[(key[k] >> shift) & 0xFFu], 1u);
+        __syncthreads();
+        if (wave == 0) {
+            uint32_t digit, above;
+            radix_digit(hist, rem, lane, digit, above);
+            if (lane == 0) { wl[273] = digit; wl[274] = above; }
+        }
+        __syncthreads();
+        rem -= wl[274];
+        prefix |= wl[273] << shift;
+        pmask |= 0xFFu << shift;
+        __syncthreads();                             // wl[273..274] read before the next pass writes
+    }
+    const uint32_t t = prefix;                       // the tile's R-th largest key
+    uint32_t cg = 0;
+#pragma unroll
+    for (int k = 0; k < kCandKeys; ++k) cg += (((okm >> k) & 1u) && key[k] > t) ? 1u : 0u;
+    const uint32_t gpre = wave_prefix(cg, lane, wtot);
+    if (lane == 0) wl[268 + wave] = wtot;
+    __syncthreads();
+    const uint32_t G = wl[268] + wl[269] + wl[270] + wl[271];   // < R
+    woff = 0;
+    for (int w = 0; w < wave; ++w) woff += wl[268 + w];
+    uint32_t pos = woff + gpre;
+#pragma unroll
+    for (int k = 0; k < kCandKeys; ++k)
+        if (((okm >> k) & 1u) && key[k] > t) cand[pos++] = key[k];
+    for (uint32_t q = (uint32_t)tid; q < R - G; q += kBlock) cand[G + q] = t;
+    if (tid == 0) *count = R;
+}
+
 // A tile is tile_rows consecutive rows of one tensor; wave w takes groups of rgroup rows,
 // groups interleaved over the four waves.
 template <int MODE, uint32_t F>
 __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, int lane, uint32_t* hist,
                                         float* awq_lds, const KArgs& ka, uint32_t& st)
 {
+    if constexpr (MODE == MODE_TCAND) {
+        uint32_t* wl = hist - 256 * wave;           // the workgroup's 4 x 256 words of LDS
+        const bool vec = (d.flags & DF_VEC) != 0;
+        if constexpr ((F & F_F32) != 0) {
+            if (d.in_dtype == IN_F32) {
+                if constexpr ((F & F_SCALAR) != 0) {
+                    if (!vec) { tile_tensor_cand<IN_F32, 1>(d, row0, wave, lane, wl, st); return; }
+                }
+                tile_tensor_cand<IN_F32, 4>(d, row0, wave, lane, wl, st);
+                return;
+            }
+        }
+        if constexpr ((F & F_BF16) != 0) {
+            if constexpr ((F & F_SCALAR) != 0) {
+                if (!vec) { tile_tensor_cand<IN_BF16, 1>(d, row0, wave, lane, wl, st); return; }
+            }
+            tile_tensor_cand<IN_BF16, 8>(d, row0, wave, lane, wl, st);
+        }
+        return;
+    }
     if constexpr (MODE == MODE_TSEL) {
         uint32_t* wg_hist = hist - 256 * wave;      // the workgroup's LDS histograms, 4 x 256 words
         const int64_t nrows = (int64_t)d.tile_rows * ka.tsel_group;   // row0 counts select tiles
@@ -1344,6 +1553,8 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
     if constexpr (is_export<MODE>) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.dq_dtype));
     if constexpr (MODE == MODE_SQWA || MODE == MODE_EMA || MODE == MODE_SWA) asm volatile("" ::"s"(d.mean));
     if constexpr (MODE == MODE_TSEL) asm volatile("" ::"s"(d.tstate), "s"(d.rank_top), "s"(d.in_dtype));
+    if constexpr (MODE == MODE_TCAND)
+        asm volatile("" ::"s"(d.tstate), "s"(d.rank_top), "s"(d.in_dtype), "s"(d.cand), "s"(d.crows), "s"(d.ccap));
     if constexpr (MODE == MODE_DECODE) asm volatile("" ::"s"(d.codes), "s"(d.scales), "s"(d.dq), "s"(d.f16_out), "s"(d.awq_out));
     if constexpr (is_export<MODE>) asm volatile("" ::"s"(d.tstate));
     if constexpr (MODE == MODE_FQ || MODE == MODE_FQ_BWD)
@@ -1358,11 +1569,13 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
 // pointers (read-only for the whole launch, so scalar loads).  F is the feature set compiled in.
 // Occupancy floor for the lean streaming variants, chosen so the register budget still needs
 // no scratch: 7 waves per SIMD (<= 72 VGPRs) for export rows, 5 (<= 96) for fp32 SQWA rows,
-// which also keep a running mean in flight.  Measured: ~1% faster each; a floor that forces
-// spilling (export at 8 waves, STE at 6) is slower.
+// which also keep a running mean in flight; 6 (<= 80 VGPRs) for the candidate pass, whose tiles
+// each make one round trip to memory.  Measured: ~1% faster each for the first two; a floor that
+// forces spilling (export at 8 waves, STE at 6) is slower.
 template <int MODE, uint32_t F>
 constexpr int kMinWaves = (MODE == MODE_EXPORT && (F == (F_F32 | F_PASS) || F == (F_BF16 | F_PASS))) ? 7 :
-                          (MODE == MODE_SQWA && F == (F_F32 | F_PASS)) ? 5 : 1;
+                          (MODE == MODE_SQWA && F == (F_F32 | F_PASS)) ? 5 :
+                          MODE == MODE_TCAND ? 6 : 1;
 
 template <int MODE, uint32_t F>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<MODE, F>)))
@@ -1393,7 +1606,8 @@ pgq_table_kernel(const TableHeader* __restrict__ hdr,
         const uint32_t ndi = next < ka.n_tiles ? tile_desc[next] : 0;
         const uint32_t first = tile_start[di];
         const Desc d = fetch_desc<MODE, F>(table + di);
-        const int64_t trows = (int64_t)d.tile_rows * (MODE == MODE_TSEL ? ka.tsel_group : 1);
+        const int64_t trows = MODE == MODE_TCAND ? (int64_t)d.crows
+                                                 : (int64_t)d.tile_rows * (MODE == MODE_TSEL ? ka.tsel_group : 1);
         do_tile<MODE, F>(d, (int64_t)(tile - first) * trows, wave, lane, hist, awq_lds, ka, st);
         tile = next;
         di = ndi;
