@@ -51,6 +51,10 @@ __device__ __forceinline__ const GLB T* gp(const T* p) { return (const GLB T*)p;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t s16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t fbits(float f) { return __float_as_uint(f); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
@@ -66,6 +70,11 @@ __device__ __forceinline__ uint16_t f2bf(float f)
 {
     __bf16 b = (__bf16)f;                      // gfx950 v_cvt_pk_bf16_f32: round to nearest even
     return __builtin_bit_cast(uint16_t, b);
+}
+// two values to bf16 in one conversion: a in bits 0..15, b in bits 16..31
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // ---- wave-wide reductions with DPP (quad swaps, row mirrors, row broadcasts), result uniform --
@@ -242,6 +251,21 @@ __device__ __forceinline__ void store_u16(GLB uint16_t* base, uint32_t e, const 
     }
 }
 
+// VEC values rounded to bf16 (nearest even), two per conversion, at element e
+template <int VEC>
+__device__ __forceinline__ void store_bf16(GLB uint16_t* base, uint32_t e, const float (&v)[VEC])
+{
+    if constexpr (VEC == 1) {
+        stnt(at<uint16_t>(base, e * 2u), f2bf(v[0]));
+    } else {
+        uint32_t w[VEC / 2];
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) w[i] = pk_bf16(v[2 * i], v[2 * i + 1]);
+        if constexpr (VEC == 4) stnt(at<u32x2>(base, e * 2u), u32x2{w[0], w[1]});
+        else stnt(at<u32x4>(base, e * 2u), u32x4{w[0], w[1], w[2], w[3]});
+    }
+}
+
 template <int VEC>
 __device__ __forceinline__ void load_u16(const GLB uint16_t* base, uint32_t e, uint16_t (&h)[VEC])
 {
@@ -398,8 +422,8 @@ struct RowCtx {
     float sf;       // fp32 value of the fp16 scale
     float rinv;     // fl32(1 / sf)
     float Qf;       // Q
-    float Qc;       // Q + 1: clamp for the reciprocal estimate
     float L;        // (Q + 1/2) * sf, exact: the STE mask is |x| <= L
+    uint32_t lt1;   // bf16 inputs: (L truncated to bf16) + 1 in both 16-bit halves
     float kf;       // SQWA snapshot index
     int k;
     int fq_mode;
@@ -410,33 +434,37 @@ __device__ __forceinline__ void set_scale(RowCtx& rc, float sf)
     rc.sf = sf;
     rc.rinv = 1.0f / sf;                                  // correctly rounded
     rc.L = ((2.0f * rc.Qf + 1.0f) * sf) * 0.5f;           // (2Q+1) * s has <= 19 bits: exact
+    // L > 0; its top 16 bits are the largest bf16 <= L, so a bf16 x has |x| <= L exactly when
+    // the bits of |x| are below lt1 (NaN bits are above every lt1, as NaN fails the comparison)
+    const uint32_t lt = (fbits(rc.L) >> 16) + 1u;
+    rc.lt1 = lt | (lt << 16);
 }
 
 // code = clamp(rne(x / s), -Q, Q), bit-identical to rounding the correctly rounded quotient:
-// y = x * fl32(1/s) is within 2^-15.9 of x / s whenever |x / s| <= Q + 2 (relative error
+// y = x * fl32(1/s) is within 2^-15 of x / s whenever |x / s| <= Q + 2 (relative error
 // <= 2^-23), so rint(y) is the nearest integer to x / s unless y lies within 2^-12 of a
-// half-integer.  A fl32 quotient can only equal a half-integer h (|h| < 2^12) when x / s == h
-// (s has 11 significant bits, x 24), so rne(fl32(x / s)) is the exact rounding of x / s.
-// Chunks with any near-tie lane are recomputed with the correctly rounded divide itself.
-// Codes are integers held in floats; zero is kept as +0 so that code * s is +0, as it is for
-// an integer code converted back to binary32.
+// half-integer.  Beyond Q + 2, y > Q + 1 and both roundings clamp to +-Q.  A fl32 quotient can
+// only equal a half-integer h (|h| < 2^12) when x / s == h (s has 11 significant bits, x 24), so
+// rne(fl32(x / s)) is the exact rounding of x / s.  Chunks with a lane whose y is within 2^-12
+// of a half-integer are recomputed with the correctly rounded divide itself.  A code may be -0
+// here; callers form code * s as fma(code, s, +0), which is +0 for either zero.  Codes of
+// non-finite inputs are unspecified (the row's status bit reports them).
 template <int VEC>
 __device__ __forceinline__ void quant_chunk(const float (&x)[VEC], const RowCtx& rc, float (&r)[VEC])
 {
-    bool near = false;
+    float dev = 0.0f;            // max |y - rint(y)| over the lane's elements, <= 1/2
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
-        float y = x[v] * rc.rinv;
-        y = __builtin_amdgcn_fmed3f(y, -rc.Qc, rc.Qc);
+        const float y = x[v] * rc.rinv;
         const float q0 = __builtin_rintf(y);
-        near |= fabsf(fabsf(y - q0) - 0.5f) < 0x1p-12f;
-        r[v] = __builtin_amdgcn_fmed3f(q0, -rc.Qf, rc.Qf) + 0.0f;   // + 0 turns a -0 code into +0
+        dev = fmaxf(dev, fabsf(y - q0));
+        r[v] = __builtin_amdgcn_fmed3f(q0, -rc.Qf, rc.Qf);
     }
-    if (__ballot(near)) {
+    if (__ballot(dev > 0.5f - 0x1p-12f)) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
             const float t = x[v] / rc.sf;
-            r[v] = fminf(fmaxf(__builtin_rintf(t), -rc.Qf), rc.Qf) + 0.0f;
+            r[v] = fminf(fmaxf(__builtin_rintf(t), -rc.Qf), rc.Qf);
         }
     }
 }
@@ -477,7 +505,7 @@ __device__ __forceinline__ RowOut row_out(const Desc& d, int64_t row)
 template <int MODE, int VEC>
 struct Aux {
     float m[MODE == MODE_SQWA ? VEC : 1];
-    uint16_t g[MODE == MODE_FQ ? VEC : 1];
+    uint32_t g[MODE == MODE_FQ && VEC == 8 ? 4 : 1];    // bf16 gradient: pairs (VEC 8) or one value
 };
 
 template <int MODE, int VEC>
@@ -487,15 +515,24 @@ __device__ __forceinline__ void load_aux(const RowOut& ro, uint32_t cu, int lane
     if constexpr (MODE == MODE_SQWA) {
         if (rc.k > 1 && valid) load_f32<VEC>(ro.mean + cu * VEC, (uint32_t)lane * VEC, ax.m);
     } else if constexpr (MODE == MODE_FQ) {
-        if (rc.fq_mode == PGQ_FQ_FWD_BWD && valid) load_u16<VEC>(ro.grad + cu * VEC, (uint32_t)lane * VEC, ax.g);
+        if (rc.fq_mode == PGQ_FQ_FWD_BWD && valid) {
+            if constexpr (VEC == 8) {
+                const u32x4 g = ldnt(at<u32x4>(ro.grad + cu * VEC, (uint32_t)lane * 16u));
+                ax.g[0] = g.x; ax.g[1] = g.y; ax.g[2] = g.z; ax.g[3] = g.w;
+            } else {
+                ax.g[0] = ldnt(at<uint16_t>(ro.grad + cu, (uint32_t)lane * 2u));
+            }
+        }
     }
 }
 
 // ---- outputs of one chunk: lane l owns VEC elements at (cu + l) * VEC of the row -------------
 // cu is uniform: it moves the scalar base pointers, and every lane adds the same small offset
-// lane * VEC, so all chunks of a row share one offset register.
+// lane * VEC, so all chunks of a row share one offset register.  xw: for bf16 inputs read eight
+// at a time, the four input words (element 2i in the low half of word i); the STE mask uses them.
 template <int MODE, bool AWQ, int VEC>
 __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const float (&x)[VEC],
+                                          const uint32_t (&xw)[VEC == 8 ? 4 : 1],
                                           const float (&a)[VEC], const float (&ainv)[VEC], bool has_awq,
                                           const RowCtx& rc, bool valid, int lane, const Aux<MODE, VEC>& ax)
 {
@@ -506,7 +543,7 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
     float dq[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
-        dq[v] = r[v] * rc.sf;                     // exact (<= 8 + 11 significant bits); +0 for code 0
+        dq[v] = __builtin_fmaf(r[v], rc.sf, 0.0f);   // exact (<= 8 + 11 significant bits); +0 for code +-0
         if constexpr (AWQ) {
             // fl32(dq / a) from the correctly rounded reciprocal ainv = fl32(1/a): one product and
             // one remainder correction (Markstein).  Exact for every numerator of <= 18 and
@@ -525,14 +562,8 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
         if (!valid) return;
         if (ro.codes) store_codes<VEC>(ro.codes + eu, e, r);
         if (ro.dq) {
-            if (ro.dq_f32) {
-                store_f32<VEC>(static_cast<GLB float*>(ro.dq) + eu, e, dq);
-            } else {
-                uint16_t h[VEC];
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) h[v] = f2bf(dq[v]);
-                store_u16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + eu, e, h);
-            }
+            if (ro.dq_f32) store_f32<VEC>(static_cast<GLB float*>(ro.dq) + eu, e, dq);
+            else store_bf16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + eu, e, dq);
         }
     } else if constexpr (MODE == MODE_SQWA) {
         if (!valid) return;
@@ -550,38 +581,45 @@ __device__ __forceinline__ void chunk_out(const RowOut& ro, uint32_t cu, const f
             store_f32<VEC>(mp, e, m);
         }
     } else if constexpr (MODE == MODE_FQ) {
-        bool keep[VEC];
+        // mask bits: bit j % 8 of byte j / 8 of the row; gradient kept where |x| <= L, else +0
+        if constexpr (VEC == 8) {
+            // per 16-bit half: (bits of |x|) - lt1 is negative exactly for the kept elements, and
+            // the arithmetic shift spreads that sign over the half
+            uint32_t km[4];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) keep[v] = fabsf(x[v]) <= rc.L;
-        // mask bits: bit j % 8 of byte j / 8 of the row
-        if (ro.mask) {
-            if constexpr (VEC == 8) {
-                if (valid) {
-                    uint32_t byte = 0;
-#pragma unroll
-                    for (int v = 0; v < 8; ++v) byte |= keep[v] ? (1u << v) : 0u;
-                    *at<uint8_t>(ro.mask + cu, (uint32_t)lane) = (uint8_t)byte;
-                }
-            } else {
+            for (int i = 0; i < 4; ++i) {
+                const u16x2 dl = __builtin_bit_cast(u16x2, xw[i] & 0x7FFF7FFFu) - __builtin_bit_cast(u16x2, rc.lt1);
+                km[i] = __builtin_bit_cast(uint32_t, (s16x2)(__builtin_bit_cast(s16x2, dl) >> (s16x2){15, 15}));
+            }
+            if (ro.mask && valid) {
+                // byte j of t (of u) is 0xFF when element j (4 + j) is kept; it gives bit j (4 + j),
+                // and the byte sum gathers the eight disjoint bits
+                const uint32_t t = __builtin_amdgcn_perm(km[1], km[0], 0x06040200u);
+                const uint32_t u = __builtin_amdgcn_perm(km[3], km[2], 0x06040200u);
+                const uint32_t bits = (t & 0x08040201u) | (u & 0x80402010u);
+                *at<uint8_t>(ro.mask + cu, (uint32_t)lane) = (uint8_t)__builtin_amdgcn_sad_u8(bits, 0u, 0u);
+            }
+            if (!valid) return;
+            if (ro.dq) store_bf16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + eu, e, dq);
+            if (ro.codes) store_codes<VEC>(ro.codes + eu, e, r);
+            if (rc.fq_mode == PGQ_FQ_FWD_BWD)
+                stnt(at<u32x4>(ro.gout + eu, e * 2u),
+                     u32x4{ax.g[0] & km[0], ax.g[1] & km[1], ax.g[2] & km[2], ax.g[3] & km[3]});
+        } else {
+            static_assert(VEC == 1, "STE rows are read 8 or 1 elements per lane");
+            const bool keep = fabsf(x[0]) <= rc.L;
+            if (ro.mask) {
                 // element c = 64 * i + lane: the 64 lanes give 8 whole mask bytes
-                const uint64_t bal = __ballot(valid && keep[0]);
+                const uint64_t bal = __ballot(valid && keep);
                 const uint32_t byte0 = cu >> 3;
                 // lane b < 8 writes byte b of the group when that byte holds an element of the row
                 const bool own = __shfl(valid ? 1 : 0, 8 * (lane & 7), 64) != 0;
                 if (lane < 8 && own) *at<uint8_t>(ro.mask + byte0, (uint32_t)lane) = (uint8_t)(bal >> (8 * lane));
             }
-        }
-        if (!valid) return;
-        uint16_t h[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) h[v] = f2bf(dq[v]);
-        if (ro.dq) store_u16<VEC>(static_cast<GLB uint16_t*>(ro.dq) + eu, e, h);
-        if (ro.codes) store_codes<VEC>(ro.codes + eu, e, r);
-        if (rc.fq_mode == PGQ_FQ_FWD_BWD) {
-            uint16_t g[VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) g[v] = keep[v] ? ax.g[v] : (uint16_t)0;
-            store_u16<VEC>(ro.gout + eu, e, g);
+            if (!valid) return;
+            if (ro.dq) store_bf16<1>(static_cast<GLB uint16_t*>(ro.dq) + eu, e, dq);
+            if (ro.codes) store_codes<1>(ro.codes + eu, e, r);
+            if (rc.fq_mode == PGQ_FQ_FWD_BWD) stnt(at<uint16_t>(ro.gout + eu, e * 2u), keep ? (uint16_t)ax.g[0] : (uint16_t)0);
         }
     }
 }
@@ -653,6 +691,90 @@ __device__ __forceinline__ void fill_awq_lds(const Desc& d, bool write_out, floa
     }
 }
 
+// One lane's VEC input elements of a chunk as binary32 values.  bf16 rows read eight at a time
+// (no AWQ) use the packed specialization below.
+template <int IN, int VEC, bool RAW>
+struct XChunk {
+    float x[VEC];
+    __device__ __forceinline__ void load(const GLB void* row, uint32_t e) { load_x<IN, VEC>(row, e, x); }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) x[v] = 0.0f;
+    }
+    __device__ __forceinline__ void unpack(float (&o)[VEC], uint32_t (&w)[VEC == 8 ? 4 : 1]) const
+    {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) o[v] = x[v];
+#pragma unroll
+        for (int i = 0; i < (VEC == 8 ? 4 : 1); ++i) w[i] = 0;      // read by the STE mask only
+    }
+    // running maximum of the magnitude bit patterns (padding is +0)
+    __device__ __forceinline__ uint32_t max_acc(uint32_t m) const
+    {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) m = max(m, fbits(x[v]) & 0x7FFFFFFFu);
+        return m;
+    }
+    __device__ __forceinline__ static uint32_t max_final(uint32_t m) { return m; }
+    template <class F>
+    __device__ __forceinline__ void keys(F&& f, bool ok) const
+    {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, ok);
+    }
+    __device__ __forceinline__ void scale(const float (&a)[VEC])
+    {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) x[v] = x[v] * a[v];
+    }
+};
+
+// Eight bf16 inputs kept as the four words they were read in (element 2i in the low half of
+// word i) until the chunk is quantized: half the registers of binary32 values, and the row
+// maximum takes one packed 16-bit max per pair (bf16 magnitudes order as their bit patterns).
+template <>
+struct XChunk<IN_BF16, 8, true> {
+    uint32_t w[4];
+    __device__ __forceinline__ void load(const GLB void* row, uint32_t e)
+    {
+        const u32x4 v = ldnt(at<u32x4>(row, e * 2u));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = 0;
+    }
+    __device__ __forceinline__ void unpack(float (&o)[8], uint32_t (&ow)[4]) const
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = bitsf(w[i] << 16);
+            o[2 * i + 1] = bitsf(w[i] & 0xFFFF0000u);
+            ow[i] = w[i];
+        }
+    }
+    // m holds two 16-bit running maxima
+    __device__ __forceinline__ uint32_t max_acc(uint32_t m) const
+    {
+        u16x2 a = __builtin_bit_cast(u16x2, m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+        return __builtin_bit_cast(uint32_t, a);
+    }
+    __device__ __forceinline__ static uint32_t max_final(uint32_t m) { return max(m & 0xFFFFu, m >> 16) << 16; }
+    template <class F>
+    __device__ __forceinline__ void keys(F&& f, bool ok) const
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f((w[i] << 16) & 0x7FFFFFFFu, ok);
+            f(w[i] & 0x7FFF0000u, ok);
+        }
+    }
+};
+
 // ---- a group of R consecutive rows of one tensor (integer kinds) ------------------------------
 // The register tile holds NCHT chunks per lane.  A row needing NCHT / R chunks or fewer is
 // processed R rows at a time: every row's loads are issued before the first reduction, so a
@@ -669,6 +791,9 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
     static_assert(NCH * R <= NCHT, "the group fits the register tile");
     static_assert(64 * NCHT * VEC == (VEC == 1 ? kRegCols_Scalar : (IN == IN_F32 ? kRegCols_F32 : kRegCols_BF16)),
                   "register tile must match the host's long-row threshold");
+    constexpr bool RAW = IN == IN_BF16 && VEC == 8 && !AWQ;
+    static_assert(MODE != MODE_FQ || VEC != 8 || RAW, "the STE mask reads the packed bf16 words");
+    using XC = XChunk<IN, VEC, RAW>;
     const int nchunk = (int)(d.cols / VEC);
     const size_t esz = IN == IN_F32 ? 4 : 2;
     const bool has_awq = AWQ && d.awq_s != nullptr;
@@ -677,14 +802,13 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
 
     RowCtx rc;
     rc.Qf = (float)d.Q;
-    rc.Qc = (float)d.Q + 1.0f;
     rc.k = ka.sqwa_k;
     rc.kf = (float)ka.sqwa_k;
     rc.fq_mode = ka.fq_mode;
 
     if (R > 1 || !LONG || nchunk <= 64 * NCH) {
         static_assert(!EXACT || !LONG, "exact-width groups never stream");
-        float x[R][NCH][VEC];
+        XC x[R][NCH];
         Aux<MODE, VEC> ax[R][NCH];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -700,12 +824,8 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 for (int i = 0; i < NCH; ++i) {
                     if (EXACT || 64 * i < nchunk) {
                         const uint32_t c = (uint32_t)(lane + 64 * i);
-                        if ((EXACT && i < NCH - 1) || (int)c < nchunk) {
-                            load_x<IN, VEC>(offset_row<IN>(wrow, 64u * i * VEC), (uint32_t)lane * VEC, x[r][i]);
-                        } else {
-#pragma unroll
-                            for (int v = 0; v < VEC; ++v) x[r][i][v] = 0.0f;
-                        }
+                        if ((EXACT && i < NCH - 1) || (int)c < nchunk) x[r][i].load(offset_row<IN>(wrow, 64u * i * VEC), (uint32_t)lane * VEC);
+                        else x[r][i].zero();
                     }
                 }
             }
@@ -719,9 +839,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                         float a[VEC];
                         lds_awq<VEC>(awq_lds, 64u * i, lane, a);
 #pragma unroll
-                        for (int r = 0; r < R; ++r)
-#pragma unroll
-                            for (int v = 0; v < VEC; ++v) x[r][i][v] = x[r][i][v] * a[v];
+                        for (int r = 0; r < R; ++r) x[r][i].scale(a);
                     }
                 }
             }
@@ -737,10 +855,8 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                     uint32_t mx = 0;
 #pragma unroll
                     for (int i = 0; i < NCH; ++i)
-                        if (EXACT || 64 * i < nchunk)
-#pragma unroll
-                            for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[r][i][v]) & 0x7FFFFFFFu);   // padding is +0
-                    mx = wave_max(mx);
+                        if (EXACT || 64 * i < nchunk) mx = x[r][i].max_acc(mx);
+                    mx = wave_max(XC::max_final(mx));
                     if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
                     ck = mx;
                     if constexpr (SEL) {
@@ -748,11 +864,8 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                             auto each = [&](auto&& f) {
 #pragma unroll
                                 for (int i = 0; i < NCH; ++i)
-                                    if (EXACT || 64 * i < nchunk) {
-                                        const bool ok = (EXACT && i < NCH - 1) || lane + 64 * i < nchunk;
-#pragma unroll
-                                        for (int v = 0; v < VEC; ++v) f(fbits(x[r][i][v]) & 0x7FFFFFFFu, ok);
-                                    }
+                                    if (EXACT || 64 * i < nchunk)
+                                        x[r][i].keys(f, (EXACT && i < NCH - 1) || lane + 64 * i < nchunk);
                             };
                             ck = kth_largest(each, d.rank_top, hist, lane);
                         }
@@ -774,7 +887,10 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                             }
                         }
                         const bool ok = (EXACT && i < NCH - 1) || (int)c < nchunk;
-                        chunk_out<MODE, AWQ, VEC>(ro, 64u * i, x[r][i], ai, yi, has_awq, rc, ok, lane, ax[r][i]);
+                        float xf[VEC];
+                        uint32_t xw[VEC == 8 ? 4 : 1];
+                        x[r][i].unpack(xf, xw);
+                        chunk_out<MODE, AWQ, VEC>(ro, 64u * i, xf, xw, ai, yi, has_awq, rc, ok, lane, ax[r][i]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -786,17 +902,17 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
         const RowOut ro = row_out(d, row);
         // cu: uniform chunk base of the piece; lane l takes chunk cu + l
-        auto load_chunk = [&](uint32_t cu, float (&x)[VEC], float (&a)[VEC], float (&ainv)[VEC],
-                              GLB uint16_t* aw) {
-            load_x<IN, VEC>(offset_row<IN>(wrow, cu * VEC), (uint32_t)lane * VEC, x);
-            if (has_awq) {
-                load_awq<VEC>(s_row, aw, cu, lane, a, ainv, st);
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) x[v] = x[v] * a[v];
-            } else {
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) { a[v] = 1.0f; ainv[v] = 1.0f; }
+        auto load_chunk = [&](uint32_t cu, XC& x, float (&a)[VEC], float (&ainv)[VEC], GLB uint16_t* aw) {
+            x.load(offset_row<IN>(wrow, cu * VEC), (uint32_t)lane * VEC);
+            if constexpr (!RAW) {
+                if (has_awq) {
+                    load_awq<VEC>(s_row, aw, cu, lane, a, ainv, st);
+                    x.scale(a);
+                    return;
+                }
             }
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) { a[v] = 1.0f; ainv[v] = 1.0f; }
         };
         uint32_t ck = 0;
         const bool tensor = (d.flags & DF_TENSOR) != 0;
@@ -807,13 +923,13 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
             for (int base = 0; base < nchunk; base += 64) {
                 const uint32_t c = (uint32_t)(base + lane);
                 if ((int)c < nchunk) {
-                    float x[VEC], a[VEC], ainv[VEC];
+                    XC x;
+                    float a[VEC], ainv[VEC];
                     load_chunk((uint32_t)base, x, a, ainv, a_out);
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) mx = max(mx, fbits(x[v]) & 0x7FFFFFFFu);
+                    mx = x.max_acc(mx);
                 }
             }
-            mx = wave_max(mx);
+            mx = wave_max(XC::max_final(mx));
             if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
             ck = mx;
         }
@@ -823,15 +939,11 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
                 auto each = [&](auto&& f) {
                     for (int base = 0; base < nchunk; base += 64) {
                         const bool ok = base + lane < nchunk;
-                        float x[VEC], a[VEC], ainv[VEC];
-                        if (ok) {
-                            load_chunk((uint32_t)base, x, a, ainv, nullptr);
-                        } else {
-#pragma unroll
-                            for (int v = 0; v < VEC; ++v) x[v] = 0.0f;
-                        }
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) f(fbits(x[v]) & 0x7FFFFFFFu, ok);
+                        XC x;
+                        float a[VEC], ainv[VEC];
+                        if (ok) load_chunk((uint32_t)base, x, a, ainv, nullptr);
+                        else x.zero();
+                        x.keys(f, ok);
                     }
                 };
                 ck = kth_largest(each, d.rank_top, hist, lane);
@@ -843,16 +955,21 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         for (int base = 0; base < nchunk; base += 64) {
             const uint32_t c = (uint32_t)(base + lane);
             const bool ok = (int)c < nchunk;
-            float x[VEC], a[VEC], ainv[VEC];
+            XC x;
+            float a[VEC], ainv[VEC];
             if (ok) {
                 load_chunk((uint32_t)base, x, a, ainv, nullptr);
             } else {
+                x.zero();
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) { x[v] = 0.0f; a[v] = 1.0f; ainv[v] = 1.0f; }
+                for (int v = 0; v < VEC; ++v) { a[v] = 1.0f; ainv[v] = 1.0f; }
             }
             Aux<MODE, VEC> ax;
             load_aux<MODE, VEC>(ro, (uint32_t)base, lane, rc, ok, ax);
-            chunk_out<MODE, AWQ, VEC>(ro, (uint32_t)base, x, a, ainv, has_awq, rc, ok, lane, ax);
+            float xf[VEC];
+            uint32_t xw[VEC == 8 ? 4 : 1];
+            x.unpack(xf, xw);
+            chunk_out<MODE, AWQ, VEC>(ro, (uint32_t)base, xf, xw, a, ainv, has_awq, rc, ok, lane, ax);
         }
     }
 }

@@ -248,6 +248,34 @@ def test_fakequant_ragged(rows, cols):
     _fq_check([w], [g], fq, 1, 2, f"{rows}x{cols}")
 
 
+@pytest.mark.parametrize("rows,cols", [(1583, 528), (7, 528), (1, 528), (13, 600), (9, 1040), (6, 2056)])
+@pytest.mark.parametrize("mode", ["fwd_bwd", "fwd_codes"])
+def test_fakequant_flat_groups(rows, cols, mode):
+    """Dense absmax STE rows of widths that leave a partial chunk instruction per row go through
+    the flattened row groups (4 rows of 528 share 5 chunk instructions); ragged last groups."""
+    say(f"STE flat groups {rows}x{cols} {mode}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    wb = oracle.f32_to_bf16((rng.standard_normal((rows, cols)) * 0.02).astype(np.float32))
+    gb = oracle.f32_to_bf16((rng.standard_normal((rows, cols)) * 1e-4).astype(np.float32))
+
+    class T:
+        pass
+    w = T(); w.data = wb; w.name = "w"
+    g = T(); g.data = gb; g.name = "g"
+    fq = ops.FakeQuant([bf16_dev(wb)], want_codes=(mode == "fwd_codes"))
+    if mode == "fwd_bwd":
+        fq.run(pgq.PGQ_FQ_FWD_BWD, [bf16_dev(gb)])
+    else:
+        fq.run(pgq.PGQ_FQ_FWD)
+    torch.cuda.synchronize()
+    _fq_check([w], [g] if mode == "fwd_bwd" else None, fq, 1, 1, f"flat {rows}x{cols}",
+              check_grad=(mode == "fwd_bwd"))
+    if mode == "fwd_codes":
+        ref = oracle.fakequant_rows(wb, 31)
+        same_bits(fq.codes[0].cpu().numpy(), ref["codes"], "flat codes")
+    assert int(fq.status.item()) == 0
+
+
 # ---------------------------------------------------------------------------------------------
 def test_config5_sqwa_full_run_sampled():
     say("config5 SQWA, 16 snapshots, final requant")
