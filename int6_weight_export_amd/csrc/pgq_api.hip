@@ -28,6 +28,7 @@ constexpr int kGroupsPerWave = 1;       // row groups per wavefront in one tile 
 constexpr int kAwqGroupsPerWave = 2;    // the same for tensors with AWQ multipliers: the workgroup
                                         // builds the multiplier table once per tile
 constexpr int kSelGroup = 3;            // export tiles per workgroup of a radix select pass
+constexpr int kFlatMaxLoads = 5;        // wave-wide loads of one flat run (STE: 8 registers each)
 constexpr uint32_t kCandMaxRank = 256;  // candidate select up to this rank from the top
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -217,6 +218,32 @@ void set_grouping(Desc& d, int mode)
             int r2 = 1;
             while (r2 * 2 <= R) r2 *= 2;
             R = r2;
+        }
+    }
+    // Flat runs (DF_FLAT): dense bf16 rows of K = cols / 8 chunks, 64 < K < 5 * 64 and K not a
+    // multiple of 64, absmax per row, no AWQ.  R rows are read as one run of IT = ceil(R K / 64)
+    // wave-wide loads; take the R <= 8 with IT <= kFlatMaxLoads that uses the loads best, when
+    // that beats ceil(K / 64) loads per row by a margin.
+    d.flags &= ~DF_FLAT;
+    if ((mode == MODE_FQ || mode == MODE_EXPORT) && (d.flags & DF_VEC) && d.in_dtype == IN_BF16 &&
+        d.kind != KIND_F16 && !d.awq_s && !(d.flags & DF_TENSOR) && d.rank_top <= 1 && d.ld == d.cols &&
+        d.cols % 8 == 0) {
+        const int64_t K = d.cols / 8;
+        if (K > 64 && K % 64 != 0 && K < 64 * kFlatMaxLoads) {
+            const double row_use = (double)K / (64.0 * (double)((K + 63) / 64));
+            int best_r = 0, best_it = 0;
+            double best_use = row_use + 0.05;
+            for (int r = 1; r <= 8; ++r) {
+                const int64_t it = (r * K + 63) / 64;
+                if (it > kFlatMaxLoads) break;
+                const double use = (double)(r * K) / (64.0 * (double)it);
+                if (use > best_use) { best_use = use; best_r = r; best_it = (int)it; }
+            }
+            if (best_r > 0) {
+                d.flags |= DF_FLAT;
+                R = best_r;
+                d.nch = best_it;
+            }
         }
     }
     d.rgroup = R;

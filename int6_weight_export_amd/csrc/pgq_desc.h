@@ -32,8 +32,10 @@ enum : uint32_t {
     DF_VEC = 1u,          // 16-byte vector path allowed for this tensor
     DF_TENSOR = 2u,       // one scale for the whole tensor, clip from its TState
     DF_PACK6 = 4u,        // codes stored 4 per 3 bytes (6-bit fields), 3 * ceil(cols / 4) per row
-    DF_CAND = 8u          // DF_TENSOR clip found from candidate keys (MODE_TCAND) instead of the
+    DF_CAND = 8u,         // DF_TENSOR clip found from candidate keys (MODE_TCAND) instead of the
                           // radix passes (MODE_TSEL)
+    DF_FLAT = 16u         // bf16 rows of cols / 8 >= 64 chunks, read rgroup rows at a time as one run
+                          // of nch wave-wide loads (dense, absmax, per row)
 };
 
 // Features a launch needs; each kernel instantiation covers a fixed set of them, and the

@@ -974,6 +974,91 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
     }
 }
 
+// ---- flat runs: R dense bf16 rows of K = cols / 8 >= 64 chunks read as one run ---------------
+// A width whose K is not a multiple of 64 leaves a partly used wave-wide load per row.  R
+// consecutive rows of a dense tensor are one contiguous run of R * K chunks, and so are their
+// outputs (codes, dequant, mask bytes, 6-bit fields, gradients), so the wave takes the run 64
+// chunks per instruction (IT instructions) and only the run's last one is partly used.  Chunk f
+// belongs to row f / K; one instruction meets at most two rows (K >= 64).  Each row's maximum
+// is a wave reduction over the lanes holding it; the row's scale parameters go to the wave's
+// LDS words, from which every lane reads those of its own row.
+template <int MODE, int IT>
+__device__ __forceinline__ void rows_flat(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* tab,
+                                          const KArgs& ka, uint32_t& st)
+{
+    using XC = XChunk<IN_BF16, 8, true>;
+    const uint32_t K = (uint32_t)(d.cols >> 3);
+    const uint32_t nvalid = (uint32_t)nrows * K;
+    const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row0 * d.cols) * 2;
+    const RowOut ro = row_out(d, row0);
+    RowCtx rc;
+    rc.Qf = (float)d.Q;
+    rc.k = ka.sqwa_k;
+    rc.kf = (float)ka.sqwa_k;
+    rc.fq_mode = ka.fq_mode;
+    XC x[IT];
+    Aux<MODE, 8> ax[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const bool ok = (uint32_t)(64 * i + lane) < nvalid;
+        load_aux<MODE, 8>(ro, 64u * i, lane, rc, ok, ax[i]);
+        if (ok) x[i].load(offset_row<IN_BF16>(wrow, 64u * 8u * i), (uint32_t)lane * 8u);
+        else x[i].zero();
+    }
+    uint32_t v[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) v[i] = XC::max_final(x[i].max_acc(0));
+    // Row maxima in run order: cur is the lane-wise maximum of row rm so far; an instruction in
+    // which row rm ends (at lane b) closes it with a wave reduction and opens row rm + 1.
+    uint32_t mrow = 0;                                    // lane j < nrows: row j's maximum
+    uint32_t cur = 0, rm = 0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const uint32_t b = (rm + 1) * K - 64u * i;        // uniform, >= 0
+        if (b < 64u) {
+            cur = max(cur, (uint32_t)lane < b ? v[i] : 0u);
+            const uint32_t m = wave_max(cur);
+            mrow = (uint32_t)lane == rm ? m : mrow;
+            ++rm;
+            cur = (uint32_t)lane < b ? 0u : v[i];
+        } else {
+            cur = max(cur, v[i]);
+        }
+    }
+    if (rm < (uint32_t)nrows) {                           // the run's last row ends with the run
+        const uint32_t m = wave_max(cur);
+        mrow = (uint32_t)lane == rm ? m : mrow;
+    }
+    // the scale parameters of all rows at once, lane j for row j
+    if (lane < nrows) {
+        if (mrow >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
+        uint16_t s16;
+        RowCtx t = rc;
+        set_scale(t, row_scale(bitsf(mrow), d.Q, s16, st));
+        if (d.scales) gp(d.scales)[row0 + lane] = s16;
+        *reinterpret_cast<u32x4*>(tab + 4 * lane) = u32x4{fbits(t.sf), fbits(t.rinv), t.lt1, 0u};
+    }
+    lds_sync_wave();
+    uint32_t ra = 0;                                      // first row met by instruction i
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        if (i > 0 && 64u * i >= (ra + 1) * K) ++ra;
+        const uint32_t f = 64u * i + (uint32_t)lane;
+        const uint32_t j = ra + (f >= (ra + 1) * K ? 1u : 0u);   // <= IT * 64 / K < 8: inside the table
+        const u32x4 p = *reinterpret_cast<const u32x4*>(tab + 4 * j);
+        RowCtx rl = rc;
+        rl.sf = bitsf(p.x);
+        rl.rinv = bitsf(p.y);
+        rl.lt1 = p.z;
+        float xf[8], a[8], ainv[8];
+        uint32_t xw[4];
+        x[i].unpack(xf, xw);
+        chunk_out<MODE, false, 8>(ro, 64u * i, xf, xw, a, ainv, false, rl, f < nvalid, lane, ax[i]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_sync_wave();                                      // table reads done before its next writes
+}
+
 // Run rows_quant with the group shape the host chose for this tensor.  Vector paths use the
 // exact chunk count (d.nch) and group size (d.rgroup); the element-wise path splits the tile.
 template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R, int NCH>
@@ -1000,6 +1085,17 @@ __device__ __forceinline__ void rows_quant_r(const Desc& d, int64_t row0, int nr
         }
         return;
     } else {
+        if constexpr (IN == IN_BF16 && VEC == 8 && (MODE == MODE_FQ || is_export<MODE>)) {
+            if (d.flags & DF_FLAT) {
+                switch (d.nch) {
+                case 2: rows_flat<MODE, 2>(d, row0, nrows, lane, hist, ka, st); break;
+                case 3: rows_flat<MODE, 3>(d, row0, nrows, lane, hist, ka, st); break;
+                case 4: rows_flat<MODE, 4>(d, row0, nrows, lane, hist, ka, st); break;
+                default: rows_flat<MODE, 5>(d, row0, nrows, lane, hist, ka, st); break;
+                }
+                return;
+            }
+        }
         // (rgroup, nch) pairs the host produces: rgroup = NCHT / pow2ceil(nch), or 1
         const int key = d.rgroup * 16 + d.nch;
         if (d.nch == 0) {            // longer than the register tile: stream row by row

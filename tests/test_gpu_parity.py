@@ -97,6 +97,32 @@ def test_ragged_bf16_input(rows, cols):
         _check_rows(oracle.bf16_to_f32(wb), out, 31, pct[0], pct[1], f"bf16 {rows}x{cols} {pct}")
 
 
+@pytest.mark.parametrize("q", [(6, 9999, 10000), (6, 1, 1)])
+def test_export_bf16_flat_runs(q):
+    """Dense bf16 rows whose width leaves a partly used wave-wide load per row (528, 600, 1040
+    columns) are exported several rows per run; ragged last runs, an int8 tensor, one-row tensors."""
+    say(f"bf16 export, flat runs, {q}")
+    rng = np.random.default_rng(78)
+    shapes = [(1583, 528), (13, 600), (9, 1040), (1, 528), (7, 528), (130, 1040)]
+    names = ["blocks.0.attn.qkv.weight", "blocks.0.mlp.fc.weight", "blocks.1.mlp.proj.weight",
+             "blocks.2.attn.proj.weight", "blocks.3.attn.proj.weight", "tok_emb.weight"]
+    bits = [oracle.f32_to_bf16((rng.standard_t(4, s) * 0.02).astype(np.float32)) for s in shapes]
+    ex = ops.Exporter([ops.ExportTensor(nm, bf16_dev(b)) for nm, b in zip(names, bits)],
+                      ops.make_policy(q_default=q, passthrough_below=0), want_dq=True)
+    ex.run()
+    ex.run()
+    torch.cuda.synchronize()
+    assert int(ex.status.item()) == 0
+    outs = ex.outputs()
+    ref = oracle.export([(nm, oracle.bf16_to_f32(b)) for nm, b in zip(names, bits)],
+                        oracle.Policy(q6=q, passthrough_below=0))
+    for o, r, nm in zip(outs, ref, names):
+        assert o["kind"] == r["kind"], (nm, o["kind"], r["kind"])
+        same_bits(o["codes"].cpu().numpy(), r["codes"], nm + " codes")
+        same_bits(u16(o["scales"]), r["scales"], nm + " scales")
+        f32_bits_equal(f32(o["dq"]).reshape(-1), r["dq"].reshape(-1), nm + " dq")
+
+
 def test_awq_single_matrix():
     say("awq single matrix")
     ts = synth.config4()
