@@ -222,20 +222,22 @@ void set_grouping(Desc& d, int mode)
     }
     // Flat runs (DF_FLAT): dense bf16 rows of K = cols / 8 chunks, 64 < K < 5 * 64 and K not a
     // multiple of 64, absmax per row, no AWQ.  R rows are read as one run of IT = ceil(R K / 64)
-    // wave-wide loads; take the R <= 8 with IT <= kFlatMaxLoads that uses the loads best, when
-    // that beats ceil(K / 64) loads per row by a margin.
+    // wave-wide loads; take the R <= 8 with IT <= kFlatMaxLoads (STE; one fewer for exports, whose
+    // kernels keep more waves per SIMD) that uses the loads best, when that beats ceil(K / 64)
+    // loads per row by a margin.
     d.flags &= ~DF_FLAT;
     if ((mode == MODE_FQ || mode == MODE_EXPORT) && (d.flags & DF_VEC) && d.in_dtype == IN_BF16 &&
         d.kind != KIND_F16 && !d.awq_s && !(d.flags & DF_TENSOR) && d.rank_top <= 1 && d.ld == d.cols &&
         d.cols % 8 == 0) {
         const int64_t K = d.cols / 8;
-        if (K > 64 && K % 64 != 0 && K < 64 * kFlatMaxLoads) {
+        const int max_loads = mode == MODE_FQ ? kFlatMaxLoads : kFlatMaxLoads - 1;
+        if (K > 64 && K % 64 != 0 && K < 64 * max_loads) {
             const double row_use = (double)K / (64.0 * (double)((K + 63) / 64));
             int best_r = 0, best_it = 0;
             double best_use = row_use + 0.05;
             for (int r = 1; r <= 8; ++r) {
                 const int64_t it = (r * K + 63) / 64;
-                if (it > kFlatMaxLoads) break;
+                if (it > max_loads) break;
                 const double use = (double)(r * K) / (64.0 * (double)it);
                 if (use > best_use) { best_use = use; best_r = r; best_it = (int)it; }
             }

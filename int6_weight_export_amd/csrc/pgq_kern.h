@@ -783,6 +783,131 @@ struct XChunk<IN_BF16, 8, true> {
 // only the last needs a per-lane bound; otherwise NCH is the tile share and chunks are guarded.
 // awq_lds: the tensor's AWQ multipliers a_j, computed once per workgroup into LDS (every
 // tensor with AWQ whose rows fit the register tile); longer rows compute them per chunk.
+template <int MODE, bool AWQ, int IN, int VEC, int R, int NCH>
+struct RowsRegs {
+    static constexpr bool RAW = IN == IN_BF16 && VEC == 8 && !AWQ;
+    XChunk<IN, VEC, RAW> x[R][NCH];
+    Aux<MODE, VEC> ax[R][NCH];
+};
+
+__device__ __forceinline__ RowCtx row_ctx(const Desc& d, const KArgs& ka)
+{
+    RowCtx rc;
+    rc.Qf = (float)d.Q;
+    rc.k = ka.sqwa_k;
+    rc.kf = (float)ka.sqwa_k;
+    rc.fq_mode = ka.fq_mode;
+    return rc;
+}
+
+// Issue every load of the group (weights and the second input stream); nothing waits for them.
+template <int MODE, bool AWQ, int IN, int VEC, int R, int NCH, bool EXACT>
+__device__ __forceinline__ void load_rows(const Desc& d, int64_t row0, int nrows, int lane, const KArgs& ka,
+                                          RowsRegs<MODE, AWQ, IN, VEC, R, NCH>& g)
+{
+    const int nchunk = (int)(d.cols / VEC);
+    const size_t esz = IN == IN_F32 ? 4 : 2;
+    const RowCtx rc = row_ctx(d, ka);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r < nrows) {
+            const RowOut ro = row_out(d, row0 + r);
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+                if (EXACT || 64 * i < nchunk)
+                    load_aux<MODE, VEC>(ro, 64u * i, lane, rc, (EXACT && i < NCH - 1) || lane + 64 * i < nchunk,
+                                        g.ax[r][i]);
+            const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)((row0 + r) * d.ld) * esz;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                if (EXACT || 64 * i < nchunk) {
+                    const uint32_t c = (uint32_t)(lane + 64 * i);
+                    if ((EXACT && i < NCH - 1) || (int)c < nchunk) g.x[r][i].load(offset_row<IN>(wrow, 64u * i * VEC), (uint32_t)lane * VEC);
+                    else g.x[r][i].zero();
+                }
+            }
+        }
+    }
+}
+
+// Clip, scale and outputs of a loaded group.
+template <int MODE, bool AWQ, bool SEL, int IN, int VEC, int R, int NCH, bool EXACT>
+__device__ __forceinline__ void quant_rows(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
+                                           const float* awq_lds, const KArgs& ka, uint32_t& st,
+                                           RowsRegs<MODE, AWQ, IN, VEC, R, NCH>& g)
+{
+    using XC = XChunk<IN, VEC, RowsRegs<MODE, AWQ, IN, VEC, R, NCH>::RAW>;
+    const int nchunk = (int)(d.cols / VEC);
+    const bool has_awq = AWQ && d.awq_s != nullptr;
+    RowCtx rc = row_ctx(d, ka);
+    if constexpr (AWQ) {
+        if (has_awq) {
+            // the column multipliers are the same for every row: read them from LDS
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                if (EXACT || 64 * i < nchunk) {
+                    float a[VEC];
+                    lds_awq<VEC>(awq_lds, 64u * i, lane, a);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) g.x[r][i].scale(a);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r < nrows) {
+            const int64_t row = row0 + r;
+            uint32_t ck;
+            if (d.flags & DF_TENSOR) {
+                ck = gp(d.tstate)->key;         // the whole-tensor clip, selected beforehand
+            } else {
+                uint32_t mx = 0;
+#pragma unroll
+                for (int i = 0; i < NCH; ++i)
+                    if (EXACT || 64 * i < nchunk) mx = g.x[r][i].max_acc(mx);
+                mx = wave_max(XC::max_final(mx));
+                if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
+                ck = mx;
+                if constexpr (SEL) {
+                    if (d.rank_top > 1) {
+                        auto each = [&](auto&& f) {
+#pragma unroll
+                            for (int i = 0; i < NCH; ++i)
+                                if (EXACT || 64 * i < nchunk)
+                                    g.x[r][i].keys(f, (EXACT && i < NCH - 1) || lane + 64 * i < nchunk);
+                        };
+                        ck = kth_largest(each, d.rank_top, hist, lane);
+                    }
+                }
+            }
+            uint16_t s16;
+            set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
+            if (lane == 0 && d.scales && (row == 0 || !(d.flags & DF_TENSOR))) gp(d.scales)[row] = s16;
+            const RowOut ro = row_out(d, row);
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                if (EXACT || 64 * i < nchunk) {
+                    const uint32_t c = (uint32_t)(lane + 64 * i);
+                    float ai[VEC], yi[VEC];
+                    if constexpr (AWQ) {
+                        if (has_awq) {
+                            lds_awq<VEC>(awq_lds, 64u * i, lane, ai);
+                            lds_awq<VEC>(awq_lds + kRegCols_F32, 64u * i, lane, yi);
+                        }
+                    }
+                    const bool ok = (EXACT && i < NCH - 1) || (int)c < nchunk;
+                    float xf[VEC];
+                    uint32_t xw[VEC == 8 ? 4 : 1];
+                    g.x[r][i].unpack(xf, xw);
+                    chunk_out<MODE, AWQ, VEC>(ro, 64u * i, xf, xw, ai, yi, has_awq, rc, ok, lane, g.ax[r][i]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
+}
+
 template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R, int NCH, bool EXACT>
 __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
                                            const float* awq_lds, const KArgs& ka, uint32_t& st)
@@ -799,103 +924,13 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
     const bool has_awq = AWQ && d.awq_s != nullptr;
     const GLB float* s_row = has_awq ? gp(d.awq_s) : nullptr;
     GLB uint16_t* a_out = (has_awq && row0 == 0 && d.awq_out) ? gp(d.awq_out) : nullptr;
-
-    RowCtx rc;
-    rc.Qf = (float)d.Q;
-    rc.k = ka.sqwa_k;
-    rc.kf = (float)ka.sqwa_k;
-    rc.fq_mode = ka.fq_mode;
+    RowCtx rc = row_ctx(d, ka);
 
     if (R > 1 || !LONG || nchunk <= 64 * NCH) {
         static_assert(!EXACT || !LONG, "exact-width groups never stream");
-        XC x[R][NCH];
-        Aux<MODE, VEC> ax[R][NCH];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (r < nrows) {
-                const RowOut ro = row_out(d, row0 + r);
-#pragma unroll
-                for (int i = 0; i < NCH; ++i)
-                    if (EXACT || 64 * i < nchunk)
-                        load_aux<MODE, VEC>(ro, 64u * i, lane, rc, (EXACT && i < NCH - 1) || lane + 64 * i < nchunk,
-                                            ax[r][i]);
-                const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)((row0 + r) * d.ld) * esz;
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    if (EXACT || 64 * i < nchunk) {
-                        const uint32_t c = (uint32_t)(lane + 64 * i);
-                        if ((EXACT && i < NCH - 1) || (int)c < nchunk) x[r][i].load(offset_row<IN>(wrow, 64u * i * VEC), (uint32_t)lane * VEC);
-                        else x[r][i].zero();
-                    }
-                }
-            }
-        }
-        if constexpr (AWQ) {
-            if (has_awq) {
-                // the column multipliers are the same for every row: read them from LDS
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    if (EXACT || 64 * i < nchunk) {
-                        float a[VEC];
-                        lds_awq<VEC>(awq_lds, 64u * i, lane, a);
-#pragma unroll
-                        for (int r = 0; r < R; ++r) x[r][i].scale(a);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (r < nrows) {
-                const int64_t row = row0 + r;
-                uint32_t ck;
-                if (d.flags & DF_TENSOR) {
-                    ck = gp(d.tstate)->key;         // the whole-tensor clip, selected beforehand
-                } else {
-                    uint32_t mx = 0;
-#pragma unroll
-                    for (int i = 0; i < NCH; ++i)
-                        if (EXACT || 64 * i < nchunk) mx = x[r][i].max_acc(mx);
-                    mx = wave_max(XC::max_final(mx));
-                    if (mx >= 0x7F800000u) st |= PGQ_DEV_NONFINITE;
-                    ck = mx;
-                    if constexpr (SEL) {
-                        if (d.rank_top > 1) {
-                            auto each = [&](auto&& f) {
-#pragma unroll
-                                for (int i = 0; i < NCH; ++i)
-                                    if (EXACT || 64 * i < nchunk)
-                                        x[r][i].keys(f, (EXACT && i < NCH - 1) || lane + 64 * i < nchunk);
-                            };
-                            ck = kth_largest(each, d.rank_top, hist, lane);
-                        }
-                    }
-                }
-                uint16_t s16;
-                set_scale(rc, row_scale(bitsf(ck), d.Q, s16, st));
-                if (lane == 0 && d.scales && (row == 0 || !(d.flags & DF_TENSOR))) gp(d.scales)[row] = s16;
-                const RowOut ro = row_out(d, row);
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    if (EXACT || 64 * i < nchunk) {
-                        const uint32_t c = (uint32_t)(lane + 64 * i);
-                        float ai[VEC], yi[VEC];
-                        if constexpr (AWQ) {
-                            if (has_awq) {
-                                lds_awq<VEC>(awq_lds, 64u * i, lane, ai);
-                                lds_awq<VEC>(awq_lds + kRegCols_F32, 64u * i, lane, yi);
-                            }
-                        }
-                        const bool ok = (EXACT && i < NCH - 1) || (int)c < nchunk;
-                        float xf[VEC];
-                        uint32_t xw[VEC == 8 ? 4 : 1];
-                        x[r][i].unpack(xf, xw);
-                        chunk_out<MODE, AWQ, VEC>(ro, 64u * i, xf, xw, ai, yi, has_awq, rc, ok, lane, ax[r][i]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-            }
-        }
+        RowsRegs<MODE, AWQ, IN, VEC, R, NCH> g;
+        load_rows<MODE, AWQ, IN, VEC, R, NCH, EXACT>(d, row0, nrows, lane, ka, g);
+        quant_rows<MODE, AWQ, SEL, IN, VEC, R, NCH, EXACT>(d, row0, nrows, lane, hist, awq_lds, ka, st, g);
     } else if constexpr (LONG && R == 1) {
         // long row: stream it in pieces; every select pass and the output pass re-read it
         const int64_t row = row0;
@@ -983,31 +1018,40 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
 // is a wave reduction over the lanes holding it; the row's scale parameters go to the wave's
 // LDS words, from which every lane reads those of its own row.
 template <int MODE, int IT>
-__device__ __forceinline__ void rows_flat(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* tab,
-                                          const KArgs& ka, uint32_t& st)
+struct FlatRegs {
+    XChunk<IN_BF16, 8, true> x[IT];
+    Aux<MODE, 8> ax[IT];
+};
+
+template <int MODE, int IT>
+__device__ __forceinline__ void load_flat(const Desc& d, int64_t row0, int nrows, int lane, const KArgs& ka,
+                                          FlatRegs<MODE, IT>& g)
+{
+    const uint32_t nvalid = (uint32_t)nrows * (uint32_t)(d.cols >> 3);
+    const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row0 * d.cols) * 2;
+    const RowOut ro = row_out(d, row0);
+    const RowCtx rc = row_ctx(d, ka);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const bool ok = (uint32_t)(64 * i + lane) < nvalid;
+        load_aux<MODE, 8>(ro, 64u * i, lane, rc, ok, g.ax[i]);
+        if (ok) g.x[i].load(offset_row<IN_BF16>(wrow, 64u * 8u * i), (uint32_t)lane * 8u);
+        else g.x[i].zero();
+    }
+}
+
+template <int MODE, int IT>
+__device__ __forceinline__ void quant_flat(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* tab,
+                                           const KArgs& ka, uint32_t& st, FlatRegs<MODE, IT>& g)
 {
     using XC = XChunk<IN_BF16, 8, true>;
     const uint32_t K = (uint32_t)(d.cols >> 3);
     const uint32_t nvalid = (uint32_t)nrows * K;
-    const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row0 * d.cols) * 2;
     const RowOut ro = row_out(d, row0);
-    RowCtx rc;
-    rc.Qf = (float)d.Q;
-    rc.k = ka.sqwa_k;
-    rc.kf = (float)ka.sqwa_k;
-    rc.fq_mode = ka.fq_mode;
-    XC x[IT];
-    Aux<MODE, 8> ax[IT];
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-        const bool ok = (uint32_t)(64 * i + lane) < nvalid;
-        load_aux<MODE, 8>(ro, 64u * i, lane, rc, ok, ax[i]);
-        if (ok) x[i].load(offset_row<IN_BF16>(wrow, 64u * 8u * i), (uint32_t)lane * 8u);
-        else x[i].zero();
-    }
+    const RowCtx rc = row_ctx(d, ka);
     uint32_t v[IT];
 #pragma unroll
-    for (int i = 0; i < IT; ++i) v[i] = XC::max_final(x[i].max_acc(0));
+    for (int i = 0; i < IT; ++i) v[i] = XC::max_final(g.x[i].max_acc(0));
     // Row maxima in run order: cur is the lane-wise maximum of row rm so far; an instruction in
     // which row rm ends (at lane b) closes it with a wave reduction and opens row rm + 1.
     uint32_t mrow = 0;                                    // lane j < nrows: row j's maximum
@@ -1052,93 +1096,158 @@ __device__ __forceinline__ void rows_flat(const Desc& d, int64_t row0, int nrows
         rl.lt1 = p.z;
         float xf[8], a[8], ainv[8];
         uint32_t xw[4];
-        x[i].unpack(xf, xw);
-        chunk_out<MODE, false, 8>(ro, 64u * i, xf, xw, a, ainv, false, rl, f < nvalid, lane, ax[i]);
+        g.x[i].unpack(xf, xw);
+        chunk_out<MODE, false, 8>(ro, 64u * i, xf, xw, a, ainv, false, rl, f < nvalid, lane, g.ax[i]);
         __builtin_amdgcn_sched_barrier(0);
     }
     lds_sync_wave();                                      // table reads done before its next writes
 }
 
+// The row groups one wavefront takes in a tile: group g starts at row first + g * step and holds
+// min(R, rows - start) rows (none once past the tensor's end).
+struct Groups {
+    int64_t first, step, rows;
+    int count, R;
+    __device__ __forceinline__ int64_t row(int g) const { return first + (int64_t)g * step; }
+    __device__ __forceinline__ int n(int g) const { return (int)min((int64_t)R, rows - row(g)); }
+};
+
+// Run a wave's groups one after another: load(regs, g) issues group g's loads, quant(regs, g)
+// consumes them.  (Loading the next group before quantizing the current one, with twice the
+// registers, and two rows per group both measured slower: more waves per SIMD beat deeper
+// queues per wave here.)
+template <class Regs, class Load, class Quant>
+__device__ __forceinline__ void over_groups(const Groups& gs, Load&& load, Quant&& quant)
+{
+    for (int g = 0; g < gs.count; ++g) {
+        if (gs.n(g) <= 0) break;
+        Regs a;
+        load(a, g);
+        quant(a, g);
+    }
+}
+
+template <int MODE, int IT>
+__device__ __forceinline__ void rows_flat(const Desc& d, const Groups& gs, int lane, uint32_t* tab, const KArgs& ka,
+                                          uint32_t& st)
+{
+    using Regs = FlatRegs<MODE, IT>;
+    over_groups<Regs>(
+        gs, [&](Regs& g, int k) { load_flat<MODE, IT>(d, gs.row(k), gs.n(k), lane, ka, g); },
+        [&](Regs& g, int k) { quant_flat<MODE, IT>(d, gs.row(k), gs.n(k), lane, tab, ka, st, g); });
+}
+
 // Run rows_quant with the group shape the host chose for this tensor.  Vector paths use the
 // exact chunk count (d.nch) and group size (d.rgroup); the element-wise path splits the tile.
-template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC, int R, int NCH>
-__device__ __forceinline__ void rows_exact(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
+template <int MODE, bool AWQ, bool SEL, int IN, int VEC, int R, int NCH>
+__device__ __forceinline__ void rows_exact(const Desc& d, const Groups& gs, int lane, uint32_t* hist,
                                            const float* awq_lds, const KArgs& ka, uint32_t& st)
 {
-    rows_quant<MODE, AWQ, SEL, false, IN, VEC, R, NCH, true>(d, row0, nrows, lane, hist, awq_lds, ka, st);
+    using Regs = RowsRegs<MODE, AWQ, IN, VEC, R, NCH>;
+    over_groups<Regs>(
+        gs, [&](Regs& g, int k) { load_rows<MODE, AWQ, IN, VEC, R, NCH, true>(d, gs.row(k), gs.n(k), lane, ka, g); },
+        [&](Regs& g, int k) {
+            quant_rows<MODE, AWQ, SEL, IN, VEC, R, NCH, true>(d, gs.row(k), gs.n(k), lane, hist, awq_lds, ka, st, g);
+        });
 }
 
 template <int MODE, bool AWQ, bool SEL, bool LONG, int IN, int VEC>
-__device__ __forceinline__ void rows_quant_r(const Desc& d, int64_t row0, int nrows, int lane, uint32_t* hist,
+__device__ __forceinline__ void rows_quant_r(const Desc& d, const Groups& gs, int lane, uint32_t* hist,
                                              const float* awq_lds, const KArgs& ka, uint32_t& st)
 {
     constexpr int NCHT = (VEC == 1) ? 16 : ((IN == IN_F32) ? 8 : 4);
     if constexpr (VEC == 1) {
-        switch (d.rgroup) {
-        case 8: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 8, NCHT / 8, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
-        case 4: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 4, NCHT / 4, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
-        case 2: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 2, NCHT / 2, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
-        default:
-            for (int r = 0; r < nrows; ++r)
-                rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, awq_lds, ka, st);
-            break;
+        for (int g = 0; g < gs.count; ++g) {
+            const int64_t row0 = gs.row(g);
+            const int nrows = gs.n(g);
+            if (nrows <= 0) break;
+            switch (d.rgroup) {
+            case 8: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 8, NCHT / 8, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
+            case 4: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 4, NCHT / 4, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
+            case 2: rows_quant<MODE, AWQ, SEL, false, IN, VEC, 2, NCHT / 2, false>(d, row0, nrows, lane, hist, awq_lds, ka, st); break;
+            default:
+                for (int r = 0; r < nrows; ++r)
+                    rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, awq_lds, ka, st);
+                break;
+            }
         }
         return;
     } else {
         if constexpr (IN == IN_BF16 && VEC == 8 && (MODE == MODE_FQ || is_export<MODE>)) {
             if (d.flags & DF_FLAT) {
                 switch (d.nch) {
-                case 2: rows_flat<MODE, 2>(d, row0, nrows, lane, hist, ka, st); break;
-                case 3: rows_flat<MODE, 3>(d, row0, nrows, lane, hist, ka, st); break;
-                case 4: rows_flat<MODE, 4>(d, row0, nrows, lane, hist, ka, st); break;
-                default: rows_flat<MODE, 5>(d, row0, nrows, lane, hist, ka, st); break;
+                case 2: rows_flat<MODE, 2>(d, gs, lane, hist, ka, st); break;
+                case 3: rows_flat<MODE, 3>(d, gs, lane, hist, ka, st); break;
+                case 4: rows_flat<MODE, 4>(d, gs, lane, hist, ka, st); break;
+                default:
+                    if constexpr (MODE == MODE_FQ) rows_flat<MODE, 5>(d, gs, lane, hist, ka, st);
+                    break;
                 }
                 return;
             }
         }
-        // (rgroup, nch) pairs the host produces: rgroup = NCHT / pow2ceil(nch), or 1
-        const int key = d.rgroup * 16 + d.nch;
         if (d.nch == 0) {            // longer than the register tile: stream row by row
             if constexpr (LONG) {
-                for (int r = 0; r < nrows; ++r)
-                    rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, row0 + r, 1, lane, hist, awq_lds, ka, st);
+                for (int g = 0; g < gs.count; ++g) {
+                    const int nrows = gs.n(g);
+                    if (nrows <= 0) break;
+                    for (int r = 0; r < nrows; ++r)
+                        rows_quant<MODE, AWQ, SEL, LONG, IN, VEC, 1, NCHT, false>(d, gs.row(g) + r, 1, lane, hist,
+                                                                                awq_lds, ka, st);
+                }
             }
             return;
         }
+        // (rgroup, nch) pairs the host produces: rgroup = NCHT / pow2ceil(nch), or 1
+        const int key = d.rgroup * 16 + d.nch;
         if constexpr (NCHT == 8) {
             switch (key) {
-            case 8 * 16 + 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 8, 1>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
-            case 4 * 16 + 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 4, 2>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
-            case 2 * 16 + 3: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 3>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
-            case 2 * 16 + 4: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 4>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
+            case 8 * 16 + 1: rows_exact<MODE, AWQ, SEL, IN, VEC, 8, 1>(d, gs, lane, hist, awq_lds, ka, st); return;
+            case 4 * 16 + 2: rows_exact<MODE, AWQ, SEL, IN, VEC, 4, 2>(d, gs, lane, hist, awq_lds, ka, st); return;
+            case 2 * 16 + 3: rows_exact<MODE, AWQ, SEL, IN, VEC, 2, 3>(d, gs, lane, hist, awq_lds, ka, st); return;
+            case 2 * 16 + 4: rows_exact<MODE, AWQ, SEL, IN, VEC, 2, 4>(d, gs, lane, hist, awq_lds, ka, st); return;
             default: break;
             }
         } else {
             switch (key) {
-            case 4 * 16 + 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 4, 1>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
-            case 2 * 16 + 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 2, 2>(d, row0, nrows, lane, hist, awq_lds, ka, st); return;
+            case 4 * 16 + 1: rows_exact<MODE, AWQ, SEL, IN, VEC, 4, 1>(d, gs, lane, hist, awq_lds, ka, st); return;
+            case 2 * 16 + 1: rows_exact<MODE, AWQ, SEL, IN, VEC, 2, 1>(d, gs, lane, hist, awq_lds, ka, st); return;
+            case 2 * 16 + 2: rows_exact<MODE, AWQ, SEL, IN, VEC, 2, 2>(d, gs, lane, hist, awq_lds, ka, st); return;
             default: break;
             }
         }
-        // one row at a time with its exact chunk count
-        for (int r = 0; r < nrows; ++r) {
-            const int64_t row = row0 + r;
-            switch (d.nch) {
-            case 1: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 1>(d, row, 1, lane, hist, awq_lds, ka, st); break;
-            case 2: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 2>(d, row, 1, lane, hist, awq_lds, ka, st); break;
-            case 3: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 3>(d, row, 1, lane, hist, awq_lds, ka, st); break;
-            case 4: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 4>(d, row, 1, lane, hist, awq_lds, ka, st); break;
-            default:
-                if constexpr (NCHT == 8) {
+        if (d.rgroup != 1) {         // any other group shape: its rows one at a time
+            for (int g = 0; g < gs.count; ++g) {
+                const int nrows = gs.n(g);
+                if (nrows <= 0) break;
+                for (int r = 0; r < nrows; ++r) {
+                    const Groups one{gs.row(g) + r, 1, d.rows, 1, 1};
                     switch (d.nch) {
-                    case 5: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 5>(d, row, 1, lane, hist, awq_lds, ka, st); break;
-                    case 6: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 6>(d, row, 1, lane, hist, awq_lds, ka, st); break;
-                    case 7: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 7>(d, row, 1, lane, hist, awq_lds, ka, st); break;
-                    default: rows_exact<MODE, AWQ, SEL, LONG, IN, VEC, 1, 8>(d, row, 1, lane, hist, awq_lds, ka, st); break;
+                    case 1: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 1>(d, one, lane, hist, awq_lds, ka, st); break;
+                    case 2: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 2>(d, one, lane, hist, awq_lds, ka, st); break;
+                    case 3: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 3>(d, one, lane, hist, awq_lds, ka, st); break;
+                    default: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 4>(d, one, lane, hist, awq_lds, ka, st); break;
                     }
                 }
-                break;
             }
+            return;
+        }
+        // one row per group with its exact chunk count
+        switch (d.nch) {
+        case 1: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 1>(d, gs, lane, hist, awq_lds, ka, st); break;
+        case 2: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 2>(d, gs, lane, hist, awq_lds, ka, st); break;
+        case 3: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 3>(d, gs, lane, hist, awq_lds, ka, st); break;
+        case 4: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 4>(d, gs, lane, hist, awq_lds, ka, st); break;
+        default:
+            if constexpr (NCHT == 8) {
+                switch (d.nch) {
+                case 5: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 5>(d, gs, lane, hist, awq_lds, ka, st); break;
+                case 6: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 6>(d, gs, lane, hist, awq_lds, ka, st); break;
+                case 7: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 7>(d, gs, lane, hist, awq_lds, ka, st); break;
+                default: rows_exact<MODE, AWQ, SEL, IN, VEC, 1, 8>(d, gs, lane, hist, awq_lds, ka, st); break;
+                }
+            }
+            break;
         }
     }
 }
@@ -1321,7 +1430,7 @@ __device__ __forceinline__ void row_decode(const Desc& d, int64_t row, int lane)
 }
 
 template <int MODE, uint32_t F>
-__device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nrows, int lane, uint32_t* hist,
+__device__ __forceinline__ void dispatch_rows(const Desc& d, const Groups& gs, int lane, uint32_t* hist,
                                               const float* awq_lds, const KArgs& ka, uint32_t& st)
 {
     constexpr bool AWQ = (F & F_AWQ) != 0;
@@ -1329,57 +1438,65 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nr
     constexpr bool LONG = (F & F_LONG) != 0;
     constexpr bool SCALAR = (F & F_SCALAR) != 0;
     const bool vec = (d.flags & DF_VEC) != 0;
+    // f(row) for every row of the wave's groups (row-wise paths)
+    auto each_row = [&](auto&& f) {
+        for (int g = 0; g < gs.count; ++g) {
+            const int nrows = gs.n(g);
+            if (nrows <= 0) break;
+            for (int r = 0; r < nrows; ++r) f(gs.row(g) + r);
+        }
+    };
     if constexpr (MODE == MODE_DECODE) {
-        for (int r = 0; r < nrows; ++r) row_decode(d, row + r, lane);
+        each_row([&](int64_t row) { row_decode(d, row, lane); });
     } else if constexpr (MODE == MODE_EMA || MODE == MODE_SWA) {
-        for (int r = 0; r < nrows; ++r) {
+        each_row([&](int64_t row) {
             if constexpr ((F & F_F32) != 0) {
                 if (d.in_dtype == IN_F32) {
                     if constexpr (SCALAR) {
-                        if (!vec) { row_average<MODE, IN_F32, 1>(d, row + r, lane, ka, st); continue; }
+                        if (!vec) { row_average<MODE, IN_F32, 1>(d, row, lane, ka, st); return; }
                     }
-                    row_average<MODE, IN_F32, 4>(d, row + r, lane, ka, st);
-                    continue;
+                    row_average<MODE, IN_F32, 4>(d, row, lane, ka, st);
+                    return;
                 }
             }
             if constexpr ((F & F_BF16) != 0) {
                 if constexpr (SCALAR) {
-                    if (!vec) { row_average<MODE, IN_BF16, 1>(d, row + r, lane, ka, st); continue; }
+                    if (!vec) { row_average<MODE, IN_BF16, 1>(d, row, lane, ka, st); return; }
                 }
-                row_average<MODE, IN_BF16, 8>(d, row + r, lane, ka, st);
+                row_average<MODE, IN_BF16, 8>(d, row, lane, ka, st);
             }
-        }
+        });
     } else if constexpr (MODE == MODE_FQ_BWD) {
-        for (int r = 0; r < nrows; ++r) {
-            if (vec) row_fq_bwd<8>(d, row + r, lane);
-            else row_fq_bwd<1>(d, row + r, lane);
-        }
+        each_row([&](int64_t row) {
+            if (vec) row_fq_bwd<8>(d, row, lane);
+            else row_fq_bwd<1>(d, row, lane);
+        });
     } else if constexpr (MODE == MODE_FQ) {
         if constexpr (SCALAR) {
-            if (!vec) { rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 1>(d, row, nrows, lane, hist, awq_lds, ka, st); return; }
+            if (!vec) { rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 1>(d, gs, lane, hist, awq_lds, ka, st); return; }
         }
-        rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 8>(d, row, nrows, lane, hist, awq_lds, ka, st);
+        rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 8>(d, gs, lane, hist, awq_lds, ka, st);
     } else {
         if constexpr ((F & F_PASS) != 0) {
             if (d.kind == KIND_F16) {
                 if constexpr ((F & F_F32) != 0) {
                     if (d.in_dtype == IN_F32) {
-                        for (int r = 0; r < nrows; ++r) {
+                        each_row([&](int64_t row) {
                             if constexpr (SCALAR) {
-                                if (!vec) { row_passthrough<MODE, IN_F32, 1>(d, row + r, lane, ka, st); continue; }
+                                if (!vec) { row_passthrough<MODE, IN_F32, 1>(d, row, lane, ka, st); return; }
                             }
-                            row_passthrough<MODE, IN_F32, 4>(d, row + r, lane, ka, st);
-                        }
+                            row_passthrough<MODE, IN_F32, 4>(d, row, lane, ka, st);
+                        });
                         return;
                     }
                 }
                 if constexpr ((F & F_BF16) != 0) {
-                    for (int r = 0; r < nrows; ++r) {
+                    each_row([&](int64_t row) {
                         if constexpr (SCALAR) {
-                            if (!vec) { row_passthrough<MODE, IN_BF16, 1>(d, row + r, lane, ka, st); continue; }
+                            if (!vec) { row_passthrough<MODE, IN_BF16, 1>(d, row, lane, ka, st); return; }
                         }
-                        row_passthrough<MODE, IN_BF16, 8>(d, row + r, lane, ka, st);
-                    }
+                        row_passthrough<MODE, IN_BF16, 8>(d, row, lane, ka, st);
+                    });
                 }
                 return;
             }
@@ -1387,17 +1504,17 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, int64_t row, int nr
         if constexpr ((F & F_F32) != 0) {
             if (d.in_dtype == IN_F32) {
                 if constexpr (SCALAR) {
-                    if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 1>(d, row, nrows, lane, hist, awq_lds, ka, st); return; }
+                    if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 1>(d, gs, lane, hist, awq_lds, ka, st); return; }
                 }
-                rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 4>(d, row, nrows, lane, hist, awq_lds, ka, st);
+                rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 4>(d, gs, lane, hist, awq_lds, ka, st);
                 return;
             }
         }
         if constexpr ((F & F_BF16) != 0) {
             if constexpr (SCALAR) {
-                if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 1>(d, row, nrows, lane, hist, awq_lds, ka, st); return; }
+                if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 1>(d, gs, lane, hist, awq_lds, ka, st); return; }
             }
-            rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 8>(d, row, nrows, lane, hist, awq_lds, ka, st);
+            rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 8>(d, gs, lane, hist, awq_lds, ka, st);
         }
     }
 }
@@ -1743,14 +1860,8 @@ __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, i
         }
     }
     const int R = d.rgroup;
-    const int groups = d.tile_rows / (kWaves * R);
-    for (int g = 0; g < groups; ++g) {
-        const int64_t first = row0 + ((int64_t)g * kWaves + wave) * R;
-        if (first < d.rows) {
-            const int nrows = (int)min((int64_t)R, d.rows - first);
-            dispatch_rows<MODE, F>(d, first, nrows, lane, hist, lds, ka, st);
-        }
-    }
+    const Groups gs{row0 + (int64_t)wave * R, (int64_t)kWaves * R, d.rows, d.tile_rows / (kWaves * R), R};
+    if (gs.n(0) > 0) dispatch_rows<MODE, F>(d, gs, lane, hist, lds, ka, st);
 }
 
 // Copy the descriptor fields a mode uses into scalar registers in one round of scalar loads.
@@ -1781,12 +1892,14 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
 // Grouped launches: descriptors come from the table in the workspace through restrict-qualified
 // pointers (read-only for the whole launch, so scalar loads).  F is the feature set compiled in.
 // Occupancy floor for the lean streaming variants, chosen so the register budget still needs
-// no scratch: 7 waves per SIMD (<= 72 VGPRs) for export rows, 5 (<= 96) for fp32 SQWA rows,
-// which also keep a running mean in flight; 6 (<= 80 VGPRs) for the candidate pass, whose tiles
-// each make one round trip to memory.  Measured: ~1% faster each for the first two; a floor that
+// no scratch: 7 waves per SIMD (<= 72 VGPRs) for fp32 export rows, 6 (<= 80) for bf16 export
+// rows (whose flat runs hold up to four loads), 5 (<= 96) for fp32 SQWA rows, which also keep a
+// running mean in flight; 6 (<= 80 VGPRs) for the candidate pass, whose tiles each make one
+// round trip to memory.  Measured: ~1% faster each for the first two; a floor that
 // forces spilling (export at 8 waves, STE at 6) is slower.
 template <int MODE, uint32_t F>
-constexpr int kMinWaves = (MODE == MODE_EXPORT && (F == (F_F32 | F_PASS) || F == (F_BF16 | F_PASS))) ? 7 :
+constexpr int kMinWaves = (MODE == MODE_EXPORT && F == (F_F32 | F_PASS)) ? 7 :
+                          (MODE == MODE_EXPORT && F == (F_BF16 | F_PASS)) ? 6 :
                           (MODE == MODE_SQWA && F == (F_F32 | F_PASS)) ? 5 :
                           MODE == MODE_TCAND ? 6 : 1;
 
