@@ -1894,14 +1894,14 @@ __device__ __forceinline__ Desc fetch_desc(const Desc* __restrict__ p)
 // Occupancy floor for the lean streaming variants, chosen so the register budget still needs
 // no scratch: 7 waves per SIMD (<= 72 VGPRs) for fp32 export rows, 6 (<= 80) for bf16 export
 // rows (whose flat runs hold up to four loads), 5 (<= 96) for fp32 SQWA rows, which also keep a
-// running mean in flight; 6 (<= 80 VGPRs) for the candidate pass, whose tiles each make one
-// round trip to memory.  Measured: ~1% faster each for the first two; a floor that
+// running mean in flight; 5 for the candidate pass, whose tiles each make one round trip to
+// memory.  Measured: ~1% faster each for the first two; a floor that
 // forces spilling (export at 8 waves, STE at 6) is slower.
 template <int MODE, uint32_t F>
 constexpr int kMinWaves = (MODE == MODE_EXPORT && F == (F_F32 | F_PASS)) ? 7 :
                           (MODE == MODE_EXPORT && F == (F_BF16 | F_PASS)) ? 6 :
                           (MODE == MODE_SQWA && F == (F_F32 | F_PASS)) ? 5 :
-                          MODE == MODE_TCAND ? 6 : 1;
+                          MODE == MODE_TCAND ? 5 : 1;
 
 template <int MODE, uint32_t F>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kMinWaves<MODE, F>)))
@@ -1915,29 +1915,23 @@ pgq_table_kernel(const TableHeader* __restrict__ hdr,
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     uint32_t* hist = hist_all[wave];
-    // round 1: the header and this tile's tensor (tile_desc lies inside the workspace whatever
-    // it holds); round 2, only for a valid table: that tensor's descriptor.  The owning tensor
-    // of the next tile (persistent grids) is fetched one tile ahead.
-    uint32_t tile = blockIdx.x;
+    // one workgroup per tile.  Round 1: the header and this tile's tensor (tile_desc lies inside
+    // the workspace whatever it holds); round 2, only for a valid table: that tensor's descriptor.
+    const uint32_t tile = blockIdx.x;
+    if (tile >= ka.n_tiles) return;
     const uint64_t magic = hdr->magic;
     const uint64_t checksum = hdr->checksum;
-    uint32_t di = tile < ka.n_tiles ? tile_desc[tile] : 0;
+    const uint32_t di = tile_desc[tile];
     if (magic != kTableMagic || checksum != ka.checksum) {
         if (threadIdx.x == 0 && ka.status) atomicOr(ka.status, PGQ_DEV_STALE_TABLE);
         return;
     }
     uint32_t st = 0;
-    while (tile < ka.n_tiles) {
-        const uint32_t next = tile + gridDim.x;
-        const uint32_t ndi = next < ka.n_tiles ? tile_desc[next] : 0;
-        const uint32_t first = tile_start[di];
-        const Desc d = fetch_desc<MODE, F>(table + di);
-        const int64_t trows = MODE == MODE_TCAND ? (int64_t)d.crows
-                                                 : (int64_t)d.tile_rows * (MODE == MODE_TSEL ? ka.tsel_group : 1);
-        do_tile<MODE, F>(d, (int64_t)(tile - first) * trows, wave, lane, hist, awq_lds, ka, st);
-        tile = next;
-        di = ndi;
-    }
+    const uint32_t first = tile_start[di];
+    const Desc d = fetch_desc<MODE, F>(table + di);
+    const int64_t trows = MODE == MODE_TCAND ? (int64_t)d.crows
+                                             : (int64_t)d.tile_rows * (MODE == MODE_TSEL ? ka.tsel_group : 1);
+    do_tile<MODE, F>(d, (int64_t)(tile - first) * trows, wave, lane, hist, awq_lds, ka, st);
     st = wave_or(st);
     if (st && lane == 0 && ka.status) atomicOr(ka.status, st);
 }
@@ -1952,8 +1946,9 @@ __global__ void __launch_bounds__(kBlock) pgq_single_kernel(const Desc d, KArgs 
     const int lane = threadIdx.x & 63;
     uint32_t* hist = hist_all[wave];
     uint32_t st = 0;
-    for (uint32_t tile = blockIdx.x; tile < ka.n_tiles; tile += gridDim.x)
-        do_tile<MODE, F>(d, (int64_t)tile * d.tile_rows, wave, lane, hist, awq_lds, ka, st);
+    const uint32_t tile = blockIdx.x;                 // one workgroup per tile
+    if (tile >= ka.n_tiles) return;
+    do_tile<MODE, F>(d, (int64_t)tile * d.tile_rows, wave, lane, hist, awq_lds, ka, st);
     st = wave_or(st);
     if (st && lane == 0 && ka.status) atomicOr(ka.status, st);
 }
