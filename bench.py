@@ -57,8 +57,9 @@ def kernel_source_hash() -> str:
 
 
 def traffic_for(mode: str):
-    """HBM bytes per launch of this mode's dominant kernel from the committed counter summary,
-    or None when there is none or the kernel sources changed since the counters were taken."""
+    """HBM bytes per step (per launch, for the single-launch modes) from the committed counter
+    summary of this mode, or None when there is none or the kernel sources changed since the
+    counters were taken."""
     path = os.path.join(PROFILES, f"traffic_{mode}.json")
     if not os.path.exists(path):
         return None
@@ -66,7 +67,123 @@ def traffic_for(mode: str):
         tr = json.load(f)
     if tr.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return tr.get("hbm_bytes_per_launch")
+    return tr.get("hbm_bytes_per_step")
+
+
+# ---- counter summaries (no GPU needed) ------------------------------------------------------
+# A profile directory holds three rocprofv3 runs of one `bench.py --mode M` command line:
+#   trace/       --kernel-trace --stats        (log: trace.log)
+#   FETCH_SIZE/  --pmc FETCH_SIZE, with --copy-calibration 6   (log: FETCH_SIZE.log)
+#   WRITE_SIZE/  --pmc WRITE_SIZE, with --copy-calibration 6   (log: WRITE_SIZE.log)
+# and commands.txt, one "pass: command" line per run.  The bench's launches are the last
+# (warmup + 2 * steps) * dispatches_per_step dispatches of the library's kernels; the counter
+# scale comes from the six 256 MiB device copies appended by --copy-calibration.
+COPY_CAL_BYTES = 256 << 20
+
+
+def _bench_line(log_path: str) -> dict:
+    with open(log_path) as f:
+        for ln in f:
+            if ln.startswith('{"metric"'):
+                return json.loads(ln)
+    raise ValueError(f"no bench line in {log_path}")
+
+
+def _csv_rows(path: str):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _step_dispatches(rows, line, key="Dispatch_Id"):
+    lib = sorted((r for r in rows if "pgq_" in r["Kernel_Name"]), key=lambda r: int(r[key]))
+    n = (line["warmup"] + 2 * line["steps"]) * line.get("dispatches_per_step", line["launches_per_step"])
+    return lib[-n:], line["warmup"] + 2 * line["steps"]
+
+
+def _short(name: str) -> str:
+    name = name.replace("pgq::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def profile_summary(d: str) -> None:
+    tl = _bench_line(os.path.join(d, "trace.log"))
+    mode = tl["mode"]
+    cmds = {}
+    with open(os.path.join(d, "commands.txt")) as f:
+        for ln in f:
+            if ":" in ln:
+                k, v = ln.split(":", 1)
+                cmds[k.strip()] = v.strip()
+    # kernel trace: durations of the step dispatches per kernel
+    tr, nsteps = _step_dispatches(_csv_rows(os.path.join(d, "trace", "run_kernel_trace.csv")), tl)
+    per = {}
+    for r in tr:
+        per.setdefault(_short(r["Kernel_Name"]), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    dom = max(per, key=lambda k: sum(per[k]))
+    kern = {k: {"launches_per_step": round(len(v) / nsteps, 3), "mean_us": round(float(np.mean(v)), 3),
+                "min_us": round(float(np.min(v)), 3), "max_us": round(float(np.max(v)), 3)} for k, v in per.items()}
+    step_us = sum(float(np.mean(v)) * len(v) / nsteps for v in per.values())
+    # counters: scale from the calibration copies, then bytes per step over the step dispatches
+    res = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cl = _bench_line(os.path.join(d, f"{c}.log"))
+        rows = _csv_rows(os.path.join(d, c, "run_counter_collection.csv"))
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        gmax = max(int(r["Grid_Size"]) for r in copies)
+        cal = [float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == gmax]
+        scale = COPY_CAL_BYTES / (float(np.mean(cal)) * 1024)
+        sd, ns = _step_dispatches(rows, cl)
+        by = {}
+        for r in sd:
+            by.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]) * 1024 * scale)
+        res[c] = {"scale": scale, "cal_kib": float(np.mean(cal)), "per_step": sum(sum(v) for v in by.values()) / ns,
+                  "per_kernel": {k: float(np.mean(v)) for k, v in by.items()}}
+    for k in kern:
+        kern[k]["fetch_bytes_per_launch"] = round(res["FETCH_SIZE"]["per_kernel"].get(k, 0.0))
+        kern[k]["write_bytes_per_launch"] = round(res["WRITE_SIZE"]["per_kernel"].get(k, 0.0))
+    alg = tl["config"]["bytes_per_step"]
+    hbm = res["FETCH_SIZE"]["per_step"] + res["WRITE_SIZE"]["per_step"]
+    out = {
+        "mode": mode, "workload": tl["config"]["workload"], "dominant_kernel": dom,
+        "kernel_source_sha256": kernel_source_hash(),
+        "kernels": kern,
+        "kernel_us_per_step": round(step_us, 3),
+        "hbm_read_bytes_per_step": round(res["FETCH_SIZE"]["per_step"]),
+        "hbm_write_bytes_per_step": round(res["WRITE_SIZE"]["per_step"]),
+        "hbm_bytes_per_step": round(hbm),
+        "algorithmic_bytes_per_step": alg,
+        "traffic_over_algorithmic": round(hbm / alg, 4),
+        "copy_calibration": {"bytes_per_copy": COPY_CAL_BYTES,
+                             "fetch_kib": round(res["FETCH_SIZE"]["cal_kib"], 1),
+                             "write_kib": round(res["WRITE_SIZE"]["cal_kib"], 1),
+                             "fetch_scale": round(res["FETCH_SIZE"]["scale"], 4),
+                             "write_scale": round(res["WRITE_SIZE"]["scale"], 4)},
+        "commands": cmds,
+    }
+    with open(os.path.join(PROFILES, f"traffic_{mode}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    md = [f"# {mode}: rocprofv3 kernel trace and HBM traffic", "",
+          f"Workload: {tl['config']['workload']}.", "",
+          "Commands (each a separate run; `<dir>` is the output directory):", "", "```"]
+    md += [f"{k}: {v}" for k, v in cmds.items()]
+    md += ["```", "",
+           f"Step launches only: the last (warmup + 2 x steps) x {tl.get('dispatches_per_step', tl['launches_per_step'])} dispatches of the "
+           "library's kernels.  Counter KiB are scaled by the readings of six 256 MiB device copies "
+           f"(FETCH_SIZE x {res['FETCH_SIZE']['scale']:.4f}, WRITE_SIZE x {res['WRITE_SIZE']['scale']:.4f}).", "",
+           "| kernel | launches / step | mean us | min us | max us | read B / launch | written B / launch |",
+           "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(kern.items(), key=lambda kv: -kv[1]["mean_us"] * kv[1]["launches_per_step"]):
+        md.append(f"| `{k}` | {v['launches_per_step']} | {v['mean_us']} | {v['min_us']} | {v['max_us']} | "
+                  f"{v['fetch_bytes_per_launch']:,} | {v['write_bytes_per_launch']:,} |")
+    md += ["", f"Kernel time per step {step_us:.3f} us.  HBM traffic per step {round(hbm):,} B "
+           f"(read {round(res['FETCH_SIZE']['per_step']):,}, written {round(res['WRITE_SIZE']['per_step']):,}) "
+           f"against {alg:,} algorithmic bytes: ratio {hbm / alg:.4f}.", "",
+           f"Kernel sources sha256: `{kernel_source_hash()}`.", ""]
+    with open(os.path.join(PROFILES, f"{mode}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(md))
+    print(json.dumps({"mode": mode, "kernel_us_per_step": round(step_us, 3), "traffic_over_algorithmic": round(hbm / alg, 4)}))
 
 
 def plan_bytes(ex, want_dq: bool) -> dict:
@@ -179,10 +296,11 @@ class Workload:
     """One bench workload: `step(i)` enqueues one step on input set i % copies."""
 
     def __init__(self, name, nbytes, rows, step, statuses, config, kernel, launches=1, timed_calls=(),
-                 flops=None, copies=1, tensors=None):
+                 flops=None, copies=1, tensors=None, dispatches=None):
         self.name, self.nbytes, self.rows = name, nbytes, rows
         self.step, self.statuses, self.config, self.kernel = step, statuses, config, kernel
         self.launches, self.timed_calls = launches, list(timed_calls)   # library calls per step
+        self.dispatches = dispatches if dispatches is not None else launches   # kernel dispatches per step
         self.flops = flops                       # a contraction: flops per step
         self.copies = copies
         self.tensors = tensors                   # host weight set (for the CPU baseline)
@@ -207,10 +325,11 @@ def _exporters(tensors, copies, torch, ops, policy=None, want_dq=True, awq=False
     return sets
 
 
-def _export_workload(name, sets, cfg, kernel, want_dq=True, tensors=None):
+def _export_workload(name, sets, cfg, kernel, want_dq=True, tensors=None, dispatches=1):
     ab = plan_bytes(sets[0], want_dq)
     return Workload(name, ab["total"], ab["rows"], lambda i: sets[i % len(sets)].run(),
-                    lambda: [int(s.status.item()) for s in sets], cfg, kernel, copies=len(sets), tensors=tensors)
+                    lambda: [int(s.status.item()) for s in sets], cfg, kernel, copies=len(sets), tensors=tensors,
+                    dispatches=dispatches)
 
 
 def workload_export(copies, torch, ops):
@@ -265,11 +384,15 @@ def workload_tensor(copies, torch, ops):
     99.99th percentile of |w| over the whole tensor (int8 tok_emb: absmax)."""
     tensors = synth.config2()
     cfg = {"workload": "per-tensor export of the 9-layer d=512 GPT weight set: one fp16 scale per tensor, "
-                       "int6 with the clip at the 99.99th percentile of |w| over the tensor (exact multi-"
-                       "workgroup select), int8 absmax tok_emb.weight, fp16 vectors, fp32 dequant",
+                       "int6 with the clip at the 99.99th percentile of |w| over the tensor (exact: candidate "
+                       "keys from one read of the tensor, one pick per tensor), int8 absmax tok_emb.weight, fp16 "
+                       "vectors, fp32 dequant",
            "tensors": len(tensors), "params": int(sum(t.numel for t in tensors))}
     sets = _exporters(tensors, copies, torch, ops, ops.make_policy(per_tensor=True))
-    return _export_workload("tensor", sets, cfg, "whole-tensor select + pick + pgq_table_kernel<0, 5u>")
+    # one call = the candidate pass, the pick and the export (every clip here has rank <= 256)
+    return _export_workload("tensor", sets, cfg, "pgq_table_kernel<9, 1u> + pgq_tensor_pick_kernel + "
+                                                 "pgq_table_kernel<0, 5u>",
+                            dispatches=3)
 
 
 def workload_fakequant(copies, torch, ops):
@@ -525,7 +648,13 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="N",
                     help="after the timed steps, run N plain device copies of 256 MiB (torch copy_) so "
                          "that hardware byte counters can be scaled against a copy of known size")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="write profiles/traffic_<mode>.json and profiles/<mode>_kernel_trace.md from the "
+                         "rocprofv3 runs in DIR (no GPU needed) and exit")
     args = ap.parse_args()
+    if args.profile_summary:
+        profile_summary(args.profile_summary)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer is "
               f"row-parallel within a GPU and this build runs no collectives)", file=sys.stderr)
@@ -561,6 +690,9 @@ def main() -> int:
         "config": config,
         "roofline": roofline(wl, m),
         "kernel": wl.kernel,
+        "mode": args.mode,
+        "launches_per_step": wl.launches,
+        "dispatches_per_step": wl.dispatches,
         "pct_of_hbm_peak": round(100 * wl.nbytes / (wall / steps) / 1e9 / HBM_PEAK_GBS, 2),
         "kernel_us_per_step": round(m["k_step_s"] * 1e6, 3),
         "kernel_us_p10_p90_per_launch": [round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
