@@ -20,6 +20,9 @@ ORC_BAD_AWQ = 8
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "orc.c")
 _LIB = os.path.join(_HERE, "liborc.so")
+# ORC_LIB names another build of orc.c to load instead (the tests' mutation and sanitizer runs);
+# it is used as given, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("ORC_LIB")
 _lock = threading.Lock()
 _lib = None
 
@@ -47,8 +50,11 @@ def load():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
-            lib = ctypes.CDLL(_LIB)
+            if _LIB_OVERRIDE:
+                lib = ctypes.CDLL(_LIB_OVERRIDE)
+            else:
+                build(force=False)
+                lib = ctypes.CDLL(_LIB)
             lib.orc_f32_to_f16_n.argtypes = [_P, _P, _I64]
             lib.orc_f32_to_bf16_n.argtypes = [_P, _P, _I64]
             lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]

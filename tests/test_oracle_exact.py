@@ -9,7 +9,10 @@ is recomputed from the definitions with fractions.Fraction:
   * the code is found by trying every integer in [-Q, Q];
   * the STE mask is |x| <= (Q + 1/2) s evaluated exactly;
   * AWQ: x' = RN32(w a), dequant = RN32(q s / a);
-  * SQWA: mean = RN32(mean + RN32(RN32(xhat - mean) / k)).
+  * SQWA: mean = RN32(mean + RN32(RN32(xhat - mean) / k));
+  * EMA: e = RN32(RN32(d e) + RN32(c w)) with d = RN32(0.997), c = RN32(1 - d), which a fused
+    multiply-add or the e + c (w - e) form would not reproduce;
+  * SWA: the SQWA running mean on the weights themselves.
 A dropped term, a wrong sign, an off-by-one rank or a wrong tie rule in the oracle
 changes at least one of these values.
 """
@@ -167,4 +170,39 @@ def test_sqwa_update_exact(orc):
             ref = xs
         else:
             ref = [ex.rn_f32(m + ex.rn_f32(ex.rn_f32(v - m) / k)) for m, v in zip(ref, xs)]
+        assert [ex.frac(v) for v in mean] == ref, k
+
+
+def test_ema_update_exact(orc):
+    """Twelve updates of 64 averages, each element recomputed in exact arithmetic and rounded
+    to binary32 after every operation of the update (Weight Averaging, decay 0.997)."""
+    rng = np.random.default_rng(6)
+    n = 64
+    e = rng.normal(0, 0.02, n).astype(np.float32)
+    e[:3] = np.float32([0.0, -0.0, 1e-39])
+    ref = [ex.frac(v) for v in e]
+    d = ex.frac(np.float32(0.997))
+    c = ex.rn_f32(1 - d)
+    assert c == ex.frac(np.float32(1.0) - np.float32(0.997))
+    for step in range(12):
+        w = (rng.normal(0, 0.02, n) * (1 + step)).astype(np.float32)
+        w[3] = np.float32(-e[3]) if step == 0 else w[3]
+        assert oracle.ema_update(e, w, 0.997) == 0
+        ref = [ex.rn_f32(ex.rn_f32(d * m) + ex.rn_f32(c * ex.frac(v))) for m, v in zip(ref, w)]
+        assert [ex.frac(v) for v in e] == ref, step
+    # an FMA-style single rounding differs from the two-product form on some element
+    fused = [ex.rn_f32(d * m + ex.rn_f32(c * ex.frac(v))) for m, v in zip(ref, w)]
+    assert fused != [ex.rn_f32(ex.rn_f32(d * m) + ex.rn_f32(c * ex.frac(v))) for m, v in zip(ref, w)]
+
+
+def test_swa_update_exact(orc):
+    rng = np.random.default_rng(7)
+    n = 64
+    mean = np.empty(n, dtype=np.float32)
+    ref = []
+    for k in range(1, 17):
+        w = rng.normal(0, 0.02, n).astype(np.float32)
+        assert oracle.swa_update(mean, w, k) == 0
+        ws = [ex.frac(v) for v in w]
+        ref = ws if k == 1 else [ex.rn_f32(m + ex.rn_f32(ex.rn_f32(v - m) / k)) for m, v in zip(ref, ws)]
         assert [ex.frac(v) for v in mean] == ref, k
