@@ -76,9 +76,11 @@ typedef enum {
 #define PGQ_DEV_BAD_AWQ     8u   /* an AWQ activation scale is <= 0 or not finite */
 #define PGQ_DEV_STALE_TABLE 16u  /* PGQ_TABLE_RESIDENT given but the workspace holds another table; nothing was written */
 
-/* Element types. */
+/* Element types.  Weight inputs may be any of the three; dequantized outputs PGQ_F32 or
+ * PGQ_BF16.  fp16 weights are widened to binary32 exactly before every step. */
 #define PGQ_F32  0
 #define PGQ_BF16 1
+#define PGQ_F16  2
 
 /* Export kinds: an integer kind is its bit width; PGQ_KIND_F16 is fp16 passthrough. */
 #define PGQ_KIND_F16 16
@@ -103,7 +105,7 @@ typedef struct {
 /* ------------------------------------------------------------------------------------------ */
 
 /* Quantize each row of a rows x cols matrix (row stride ld elements, ld >= cols).
- *   w         input, PGQ_F32 or PGQ_BF16 (w_dtype)
+ *   w         input, PGQ_F32, PGQ_BF16 or PGQ_F16 (w_dtype)
  *   awq_s     NULL, or cols fp32 activation scales s_j > 0: the row is multiplied by
  *             a_j = fp16(sqrt(s_j)) before quantization and divided by it in dequant
  *   awq_mult  NULL, or cols fp16 outputs (bit patterns) receiving a_j
@@ -159,7 +161,7 @@ pgq_status pgq_fakequant_fwd_bwd(int32_t mode, const pgq_fq_tensor* t, int32_t n
 typedef struct {
     const char* name;       /* host string used by the policy (NULL = "") */
     const void* w;          /* device input, rows x cols, row stride ld */
-    int32_t dtype;          /* PGQ_F32 or PGQ_BF16 */
+    int32_t dtype;          /* PGQ_F32, PGQ_BF16 or PGQ_F16 */
     int32_t reserved;
     int64_t rows, cols, ld; /* 1-D tensors: rows = 1; higher ranks: rows = shape[0] */
     const float* awq_s;     /* NULL or cols fp32 activation scales (used for integer kinds whose

@@ -64,6 +64,8 @@ uint64_t table_hash(const void* data, size_t n, uint64_t h)
 }
 
 size_t esize(int32_t dt) { return dt == PGQ_F32 ? 4 : 2; }
+bool weight_dtype_ok(int32_t dt) { return dt == PGQ_F32 || dt == PGQ_BF16 || dt == PGQ_F16; }
+int32_t in_of(int32_t dt) { return dt == PGQ_F32 ? IN_F32 : dt == PGQ_F16 ? IN_F16 : IN_BF16; }
 
 bool shape_ok(int64_t rows, int64_t cols, int64_t ld)
 {
@@ -96,7 +98,7 @@ void set_vec_flag(Desc& d)
 uint32_t features_of(const Desc& d)
 {
     if (d.rows <= 0 || d.cols <= 0) return 0;
-    uint32_t f = d.in_dtype == IN_F32 ? F_F32 : F_BF16;
+    uint32_t f = d.in_dtype == IN_F32 ? F_F32 : d.in_dtype == IN_F16 ? F_F16 : F_BF16;
     const bool vec = (d.flags & DF_VEC) != 0;
     if (!vec) f |= F_SCALAR;
     if (d.kind == KIND_F16) return f | F_PASS;
@@ -111,7 +113,8 @@ uint32_t features_of(const Desc& d)
 uint32_t features_avg(const Desc& d)
 {
     if (d.rows <= 0 || d.cols <= 0) return 0;
-    return (d.in_dtype == IN_F32 ? F_F32 : F_BF16) | ((d.flags & DF_VEC) ? 0u : F_SCALAR);
+    return (d.in_dtype == IN_F32 ? F_F32 : d.in_dtype == IN_F16 ? F_F16 : F_BF16) |
+           ((d.flags & DF_VEC) ? 0u : F_SCALAR);
 }
 
 Desc blank_desc()
@@ -470,7 +473,7 @@ bool name_matches(const char* name, const pgq_policy* pol)
 pgq_status check_tensor_in(const pgq_tensor_in& t)
 {
     if (!shape_ok(t.rows, t.cols, t.ld)) return PGQ_ERR_SHAPE;
-    if (t.dtype != PGQ_F32 && t.dtype != PGQ_BF16) return PGQ_ERR_DTYPE;
+    if (!weight_dtype_ok(t.dtype)) return PGQ_ERR_DTYPE;
     if (t.rows > 0 && t.cols > 0 && !t.w) return PGQ_ERR_NULL;
     if (t.w && !aligned(t.w, esize(t.dtype))) return PGQ_ERR_ALIGN;
     if (t.awq_s && !aligned(t.awq_s, 4)) return PGQ_ERR_ALIGN;
@@ -488,7 +491,7 @@ pgq_status average_descs(const pgq_tensor_in* w, int32_t n, float* const* state,
         if (w[i].awq_s) return PGQ_ERR_PARAM;
         Desc& d = descs[i];
         d.w = w[i].w;
-        d.in_dtype = w[i].dtype == PGQ_F32 ? IN_F32 : IN_BF16;
+        d.in_dtype = in_of(w[i].dtype);
         d.rows = w[i].rows;
         d.cols = w[i].cols;
         d.ld = w[i].ld;
@@ -520,7 +523,7 @@ pgq_status export_desc(const pgq_tensor_in& t, const pgq_tensor_plan& p, uint8_t
     d.rows = t.rows;
     d.cols = t.cols;
     d.ld = t.ld;
-    d.in_dtype = t.dtype == PGQ_F32 ? IN_F32 : IN_BF16;
+    d.in_dtype = in_of(t.dtype);
     d.dq_dtype = IN_F32;
     const int64_t numel = t.rows * t.cols;
     if (p.kind == PGQ_KIND_F16) {
@@ -650,7 +653,7 @@ pgq_status pgq_quantize_rows(const void* w, int32_t w_dtype, int64_t rows, int64
                              uint32_t* dev_status, void* stream)
 {
     if (!shape_ok(rows, cols, ld)) return PGQ_ERR_SHAPE;
-    if (w_dtype != PGQ_F32 && w_dtype != PGQ_BF16) return PGQ_ERR_DTYPE;
+    if (!weight_dtype_ok(w_dtype)) return PGQ_ERR_DTYPE;
     if (dq && dq_dtype != PGQ_F32 && dq_dtype != PGQ_BF16) return PGQ_ERR_DTYPE;
     if (!qparams_ok(qp)) return PGQ_ERR_PARAM;
     if (rows == 0) return PGQ_OK;
@@ -673,7 +676,7 @@ pgq_status pgq_quantize_rows(const void* w, int32_t w_dtype, int64_t rows, int64
     d.kind = qp.bits;
     d.Q = (1 << (qp.bits - 1)) - 1;
     d.rank_top = rank_top(cols, qp.pct_num, qp.pct_den);
-    d.in_dtype = w_dtype == PGQ_F32 ? IN_F32 : IN_BF16;
+    d.in_dtype = in_of(w_dtype);
     d.dq_dtype = dq_dtype == PGQ_F32 ? IN_F32 : IN_BF16;
     set_vec_flag(d);
     set_grouping(d, MODE_EXPORT);

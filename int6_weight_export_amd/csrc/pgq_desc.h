@@ -26,7 +26,7 @@ enum Mode : int32_t {
 constexpr int kModes = 10;
 template <int M>
 constexpr bool is_export = M == MODE_EXPORT || M == MODE_EXPORT6;
-enum : int32_t { IN_F32 = 0, IN_BF16 = 1 };
+enum : int32_t { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2 };
 enum : int32_t { KIND_F16 = 16 };
 enum : uint32_t {
     DF_VEC = 1u,          // 16-byte vector path allowed for this tensor
@@ -49,7 +49,8 @@ enum : uint32_t {
     F_SEL = 16u,      // clip below the row maximum (percentile select)
     F_SCALAR = 32u,   // unaligned tensors (element-wise path)
     F_LONG = 64u,     // rows longer than the register tile
-    F_ALL = 127u
+    F_F16 = 128u,     // fp16 inputs
+    F_ALL = 255u
 };
 
 // State of one tensor's whole-tensor clip select, in the caller's workspace.
@@ -85,7 +86,7 @@ struct alignas(16) Desc {
     int64_t rank_top;         // the clip is the rank_top-th largest |x| of the row (1 = max)
     int32_t kind;             // code bits, or KIND_F16
     int32_t Q;                // 2^(bits-1) - 1
-    int32_t in_dtype;         // IN_F32 / IN_BF16
+    int32_t in_dtype;         // IN_F32 / IN_BF16 / IN_F16
     int32_t dq_dtype;         // IN_F32 / IN_BF16
     uint32_t flags;           // DF_*
     int32_t rgroup;           // rows a wave processes together (1, 2, 4 or 8)

@@ -149,6 +149,17 @@ __device__ __forceinline__ void load_x(const GLB void* row, uint32_t e, float (&
             static_assert(VEC == 1, "fp32 path uses VEC 4 or 1");
             x[0] = ld(at<float>(row, e * 4u));
         }
+    } else if constexpr (IN == IN_F16) {
+        // fp16 -> binary32 is exact (v_cvt_f32_f16 keeps subnormals, infinities and NaN)
+        if constexpr (VEC == 8) {
+            const u32x4 v = ld(at<u32x4>(row, e * 2u));
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { x[2 * i] = h2f((uint16_t)(w[i] & 0xFFFFu)); x[2 * i + 1] = h2f((uint16_t)(w[i] >> 16)); }
+        } else {
+            static_assert(VEC == 1, "fp16 path uses VEC 8 or 1");
+            x[0] = h2f(ld(at<uint16_t>(row, e * 2u)));
+        }
     } else {
         if constexpr (VEC == 8) {
             const u32x4 v = ld(at<u32x4>(row, e * 2u));
@@ -1429,6 +1440,34 @@ __device__ __forceinline__ void row_decode(const Desc& d, int64_t row, int lane)
     }
 }
 
+// f(In<IN, VEC>()) for the tensor's input type among those the variant F compiles in: the
+// 16-byte vector width, or element-wise (VEC 1) for tensors off the vector path (F_SCALAR).
+template <int IN_, int VEC_>
+struct In {
+    static constexpr int IN = IN_;
+    static constexpr int VEC = VEC_;
+};
+
+template <uint32_t F, class Fn>
+__device__ __forceinline__ void with_input(const Desc& d, Fn&& f)
+{
+    const bool vec = (d.flags & DF_VEC) != 0;
+    auto pick = [&](auto in) {
+        constexpr int IN = decltype(in)::IN;
+        if constexpr ((F & F_SCALAR) != 0) {
+            if (!vec) { f(In<IN, 1>()); return; }
+        }
+        f(In<IN, IN == IN_F32 ? 4 : 8>());
+    };
+    if constexpr ((F & F_F32) != 0) {
+        if (d.in_dtype == IN_F32) { pick(In<IN_F32, 0>()); return; }
+    }
+    if constexpr ((F & F_F16) != 0) {
+        if (d.in_dtype == IN_F16) { pick(In<IN_F16, 0>()); return; }
+    }
+    if constexpr ((F & F_BF16) != 0) pick(In<IN_BF16, 0>());
+}
+
 template <int MODE, uint32_t F>
 __device__ __forceinline__ void dispatch_rows(const Desc& d, const Groups& gs, int lane, uint32_t* hist,
                                               const float* awq_lds, const KArgs& ka, uint32_t& st)
@@ -1449,22 +1488,9 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, const Groups& gs, i
     if constexpr (MODE == MODE_DECODE) {
         each_row([&](int64_t row) { row_decode(d, row, lane); });
     } else if constexpr (MODE == MODE_EMA || MODE == MODE_SWA) {
-        each_row([&](int64_t row) {
-            if constexpr ((F & F_F32) != 0) {
-                if (d.in_dtype == IN_F32) {
-                    if constexpr (SCALAR) {
-                        if (!vec) { row_average<MODE, IN_F32, 1>(d, row, lane, ka, st); return; }
-                    }
-                    row_average<MODE, IN_F32, 4>(d, row, lane, ka, st);
-                    return;
-                }
-            }
-            if constexpr ((F & F_BF16) != 0) {
-                if constexpr (SCALAR) {
-                    if (!vec) { row_average<MODE, IN_BF16, 1>(d, row, lane, ka, st); return; }
-                }
-                row_average<MODE, IN_BF16, 8>(d, row, lane, ka, st);
-            }
+        with_input<F>(d, [&](auto in) {
+            using I = decltype(in);
+            each_row([&](int64_t row) { row_average<MODE, I::IN, I::VEC>(d, row, lane, ka, st); });
         });
     } else if constexpr (MODE == MODE_FQ_BWD) {
         each_row([&](int64_t row) {
@@ -1472,6 +1498,7 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, const Groups& gs, i
             else row_fq_bwd<1>(d, row, lane);
         });
     } else if constexpr (MODE == MODE_FQ) {
+        // STE rows are bf16
         if constexpr (SCALAR) {
             if (!vec) { rows_quant_r<MODE_FQ, false, SEL, LONG, IN_BF16, 1>(d, gs, lane, hist, awq_lds, ka, st); return; }
         }
@@ -1479,43 +1506,17 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, const Groups& gs, i
     } else {
         if constexpr ((F & F_PASS) != 0) {
             if (d.kind == KIND_F16) {
-                if constexpr ((F & F_F32) != 0) {
-                    if (d.in_dtype == IN_F32) {
-                        each_row([&](int64_t row) {
-                            if constexpr (SCALAR) {
-                                if (!vec) { row_passthrough<MODE, IN_F32, 1>(d, row, lane, ka, st); return; }
-                            }
-                            row_passthrough<MODE, IN_F32, 4>(d, row, lane, ka, st);
-                        });
-                        return;
-                    }
-                }
-                if constexpr ((F & F_BF16) != 0) {
-                    each_row([&](int64_t row) {
-                        if constexpr (SCALAR) {
-                            if (!vec) { row_passthrough<MODE, IN_BF16, 1>(d, row, lane, ka, st); return; }
-                        }
-                        row_passthrough<MODE, IN_BF16, 8>(d, row, lane, ka, st);
-                    });
-                }
+                with_input<F>(d, [&](auto in) {
+                    using I = decltype(in);
+                    each_row([&](int64_t row) { row_passthrough<MODE, I::IN, I::VEC>(d, row, lane, ka, st); });
+                });
                 return;
             }
         }
-        if constexpr ((F & F_F32) != 0) {
-            if (d.in_dtype == IN_F32) {
-                if constexpr (SCALAR) {
-                    if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 1>(d, gs, lane, hist, awq_lds, ka, st); return; }
-                }
-                rows_quant_r<MODE, AWQ, SEL, LONG, IN_F32, 4>(d, gs, lane, hist, awq_lds, ka, st);
-                return;
-            }
-        }
-        if constexpr ((F & F_BF16) != 0) {
-            if constexpr (SCALAR) {
-                if (!vec) { rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 1>(d, gs, lane, hist, awq_lds, ka, st); return; }
-            }
-            rows_quant_r<MODE, AWQ, SEL, LONG, IN_BF16, 8>(d, gs, lane, hist, awq_lds, ka, st);
-        }
+        with_input<F>(d, [&](auto in) {
+            using I = decltype(in);
+            rows_quant_r<MODE, AWQ, SEL, LONG, I::IN, I::VEC>(d, gs, lane, hist, awq_lds, ka, st);
+        });
     }
 }
 
@@ -1803,43 +1804,19 @@ __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, i
 {
     if constexpr (MODE == MODE_TCAND) {
         uint32_t* wl = hist - 256 * wave;           // the workgroup's 4 x 256 words of LDS
-        const bool vec = (d.flags & DF_VEC) != 0;
-        if constexpr ((F & F_F32) != 0) {
-            if (d.in_dtype == IN_F32) {
-                if constexpr ((F & F_SCALAR) != 0) {
-                    if (!vec) { tile_tensor_cand<IN_F32, 1>(d, row0, wave, lane, wl, st); return; }
-                }
-                tile_tensor_cand<IN_F32, 4>(d, row0, wave, lane, wl, st);
-                return;
-            }
-        }
-        if constexpr ((F & F_BF16) != 0) {
-            if constexpr ((F & F_SCALAR) != 0) {
-                if (!vec) { tile_tensor_cand<IN_BF16, 1>(d, row0, wave, lane, wl, st); return; }
-            }
-            tile_tensor_cand<IN_BF16, 8>(d, row0, wave, lane, wl, st);
-        }
+        with_input<F>(d, [&](auto in) {
+            using I = decltype(in);
+            tile_tensor_cand<I::IN, I::VEC>(d, row0, wave, lane, wl, st);
+        });
         return;
     }
     if constexpr (MODE == MODE_TSEL) {
         uint32_t* wg_hist = hist - 256 * wave;      // the workgroup's LDS histograms, 4 x 256 words
         const int64_t nrows = (int64_t)d.tile_rows * ka.tsel_group;   // row0 counts select tiles
-        const bool vec = (d.flags & DF_VEC) != 0;
-        if constexpr ((F & F_F32) != 0) {
-            if (d.in_dtype == IN_F32) {
-                if constexpr ((F & F_SCALAR) != 0) {
-                    if (!vec) { tile_tensor_select<IN_F32, 1>(d, row0, nrows, wave, lane, wg_hist, ka, st); return; }
-                }
-                tile_tensor_select<IN_F32, 4>(d, row0, nrows, wave, lane, wg_hist, ka, st);
-                return;
-            }
-        }
-        if constexpr ((F & F_BF16) != 0) {
-            if constexpr ((F & F_SCALAR) != 0) {
-                if (!vec) { tile_tensor_select<IN_BF16, 1>(d, row0, nrows, wave, lane, wg_hist, ka, st); return; }
-            }
-            tile_tensor_select<IN_BF16, 8>(d, row0, nrows, wave, lane, wg_hist, ka, st);
-        }
+        with_input<F>(d, [&](auto in) {
+            using I = decltype(in);
+            tile_tensor_select<I::IN, I::VEC>(d, row0, nrows, wave, lane, wg_hist, ka, st);
+        });
         return;
     }
     // AWQ multipliers for the whole tile, once (rows that fit the register tile read them from
@@ -1961,11 +1938,11 @@ const void* kernel_ptr(bool table)
 }
 
 // Instantiations per mode, leanest first; the last covers every feature.
-constexpr uint32_t kExportVariants[] = {F_F32 | F_PASS, F_BF16 | F_PASS, F_F32 | F_PASS | F_AWQ,
+constexpr uint32_t kExportVariants[] = {F_F32 | F_PASS, F_BF16 | F_PASS, F_F16 | F_PASS, F_F32 | F_PASS | F_AWQ,
                                         F_F32 | F_PASS | F_SEL, F_ALL};
 constexpr uint32_t kFqVariants[] = {F_BF16, F_BF16 | F_SEL, F_ALL};
-constexpr uint32_t kAvgAll = F_F32 | F_BF16 | F_SCALAR;   // also the whole-tensor select's
-constexpr uint32_t kAvgVariants[] = {F_F32, F_BF16, kAvgAll};
+constexpr uint32_t kAvgAll = F_F32 | F_BF16 | F_F16 | F_SCALAR;   // also the whole-tensor select's
+constexpr uint32_t kAvgVariants[] = {F_F32, F_BF16, F_F16, kAvgAll};
 
 // Weight averaging and the whole-tensor select run as grouped launches only.
 template <int MODE>
@@ -1975,15 +1952,19 @@ const void* average_kernel(uint32_t v, bool table)
     switch (v) {
     case F_F32: return reinterpret_cast<const void*>(&pgq_table_kernel<MODE, F_F32>);
     case F_BF16: return reinterpret_cast<const void*>(&pgq_table_kernel<MODE, F_BF16>);
+    case F_F16: return reinterpret_cast<const void*>(&pgq_table_kernel<MODE, F_F16>);
     default: return reinterpret_cast<const void*>(&pgq_table_kernel<MODE, kAvgAll>);
     }
 }
 
 // The export-like modes' instantiations are spread over four translation units each (their
-// kernels dominate the build): the lean streaming variants (fp32 or bf16 input with
+// kernels dominate the build): the lean streaming variants (fp32, bf16 or fp16 input with
 // passthrough, AWQ), the percentile-select variant, and the variant with every feature (grouped
 // and single-matrix launches apart).
-constexpr bool is_lean_variant(uint32_t v) { return v == (F_F32 | F_PASS) || v == (F_BF16 | F_PASS) || v == (F_F32 | F_PASS | F_AWQ); }
+constexpr bool is_lean_variant(uint32_t v)
+{
+    return v == (F_F32 | F_PASS) || v == (F_BF16 | F_PASS) || v == (F_F16 | F_PASS) || v == (F_F32 | F_PASS | F_AWQ);
+}
 
 template <int MODE>
 const void* export_like_lean(uint32_t v, bool table)
@@ -1991,6 +1972,7 @@ const void* export_like_lean(uint32_t v, bool table)
     switch (v) {
     case F_F32 | F_PASS: return kernel_ptr<MODE, F_F32 | F_PASS>(table);
     case F_BF16 | F_PASS: return kernel_ptr<MODE, F_BF16 | F_PASS>(table);
+    case F_F16 | F_PASS: return kernel_ptr<MODE, F_F16 | F_PASS>(table);
     case F_F32 | F_PASS | F_AWQ: return kernel_ptr<MODE, F_F32 | F_PASS | F_AWQ>(table);
     default: return nullptr;
     }

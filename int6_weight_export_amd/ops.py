@@ -30,6 +30,8 @@ def _dtype_code(dt: torch.dtype) -> int:
         return pgq.PGQ_F32
     if dt == torch.bfloat16:
         return pgq.PGQ_BF16
+    if dt == torch.float16:
+        return pgq.PGQ_F16
     raise TypeError(f"unsupported dtype {dt}")
 
 
@@ -58,7 +60,7 @@ def quantize_rows(w: torch.Tensor, bits: int = 6, pct: Tuple[int, int] = (1, 1),
                   awq_s: Optional[torch.Tensor] = None, want_codes: bool = True,
                   dq_dtype: Optional[torch.dtype] = torch.float32,
                   status: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
-    """Per-row quantization of one matrix (fp32 or bf16, rows contiguous)."""
+    """Per-row quantization of one matrix (fp32, bf16 or fp16, rows contiguous)."""
     rows, cols, ld = _rows_view(w)
     dev = w.device
     if out is None:
@@ -293,7 +295,7 @@ class Sqwa:
 
 
 class _Averager:
-    """fp32 averages of a fixed list of weight tensors (fp32 or bf16, rows contiguous), updated
+    """fp32 averages of a fixed list of weight tensors (fp32, bf16 or fp16, rows contiguous), updated
     in place by one grouped launch per call.  The tensor array and the workspace holding the
     uploaded descriptor table are kept per weight buffer set, so calls over resident weights
     only re-enqueue the kernel."""

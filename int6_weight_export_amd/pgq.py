@@ -30,6 +30,7 @@ PGQ_DEV_STALE_TABLE = 16
 
 PGQ_F32 = 0
 PGQ_BF16 = 1
+PGQ_F16 = 2
 PGQ_KIND_F16 = 16
 PGQ_TABLE_RESIDENT = 1
 

@@ -14,6 +14,11 @@ def bf16_dev(bits: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
 
 
+def f16_dev(bits: np.ndarray) -> torch.Tensor:
+    """fp16 bit patterns (uint16) as a device float16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.float16)
+
+
 def u16(t: torch.Tensor) -> np.ndarray:
     if t.dtype in (torch.bfloat16, torch.float16):
         t = t.view(torch.int16)

@@ -56,6 +56,9 @@ def q(bits=6, num=1, den=1):
     (dict(qp=q(6, 3, 2)), pgq.PGQ_ERR_PARAM),
     (dict(w_dtype=5), pgq.PGQ_ERR_DTYPE),
     (dict(dq=FAKE, dq_dtype=9), pgq.PGQ_ERR_DTYPE),
+    (dict(dq=FAKE, dq_dtype=pgq.PGQ_F16), pgq.PGQ_ERR_DTYPE),     # fp16 is a weight type, not an output
+    (dict(w_dtype=pgq.PGQ_F16, rows=0), pgq.PGQ_OK),                # fp16 weights pass validation
+    (dict(w_dtype=pgq.PGQ_F16, w=FAKE + 1), pgq.PGQ_ERR_ALIGN),
     (dict(scales=None), pgq.PGQ_ERR_NULL),
     (dict(w=None), pgq.PGQ_ERR_NULL),
     (dict(awq_mult=FAKE), pgq.PGQ_ERR_NULL),
@@ -204,6 +207,24 @@ def test_average_argument_errors():
     arr[1].awq_s = 0
     arr[3].dtype = 9
     assert swa(arr, 4, st, 2, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_DTYPE
+
+
+def test_constants_match_the_header(tmp_path):
+    """The binding's copies of the header's #defines (element types, kinds, flags, status bits)."""
+    import subprocess
+    names = [n for n in dir(pgq) if n.startswith(("PGQ_F", "PGQ_BF", "PGQ_KIND", "PGQ_TABLE", "PGQ_DEV_", "PGQ_FQ_"))
+             and isinstance(getattr(pgq, n), int)]
+    assert {"PGQ_F32", "PGQ_BF16", "PGQ_F16"} <= set(names)
+    lines = ['#include <stdio.h>', f'#include "{HEADER}"', 'int main(void) {']
+    lines += [f'printf("{n} %lld\\n", (long long)({n}));' for n in names]
+    lines.append("return 0; }")
+    src, exe = tmp_path / "consts.c", tmp_path / "consts"
+    src.write_text("\n".join(lines))
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    for line in filter(None, out):
+        n, v = line.split()
+        assert getattr(pgq, n) == int(v), line
 
 
 def test_struct_layouts_match_the_header(tmp_path):

@@ -19,7 +19,7 @@ if not torch.cuda.is_available():
 import oracle  # noqa: E402
 import synth  # noqa: E402
 from int6_weight_export_amd import ops, pgq  # noqa: E402
-from tests.gpu_util import bf16_dev, dev, f32_bits_equal  # noqa: E402
+from tests.gpu_util import bf16_dev, dev, f16_dev, f32_bits_equal  # noqa: E402
 
 
 def say(msg):
@@ -61,6 +61,31 @@ def test_ema_resident_table_and_bf16_weights():
     torch.cuda.synchronize()
     ref, _ = oracle.ema_run([[oracle.bf16_to_f32(b) for b in ws] for ws in sets], 0.997)
     _check(ema.avg, ref, "ema bf16")
+
+
+def test_ema_and_swa_fp16_weights():
+    """fp16 weights (widened exactly): EMA over three steps and SWA over three checkpoints, with a
+    ragged and an odd-width tensor beside 528-wide ones."""
+    say("EMA / SWA fp16 weights")
+    shapes = [(528, 528), (70, 1000), (9, 37)]
+    rng = np.random.default_rng(6)
+    sets = [[oracle.f32_to_f16((rng.standard_normal(s) * 0.02).astype(np.float32)) for s in shapes]
+            for _ in range(3)]
+    ema = ops.Ema([f16_dev(h) for h in sets[0]], decay=0.997)
+    for s, ws in enumerate(sets):
+        ema.update([f16_dev(h) for h in ws], init=(s == 0), reuse_table=False)
+    torch.cuda.synchronize()
+    ref, st = oracle.ema_run([[oracle.f16_to_f32(h) for h in ws] for ws in sets], 0.997)
+    assert int(ema.status.item()) == st == 0
+    _check(ema.avg, ref, "ema f16")
+    swa = ops.Swa([f16_dev(h) for h in sets[0]])
+    means = [np.empty(s, dtype=np.float32) for s in shapes]
+    for k, ws in enumerate(sets, start=1):
+        swa.accumulate([f16_dev(h) for h in ws], k, reuse_table=False)
+        for m, h in zip(means, ws):
+            oracle.swa_update(m.reshape(-1), oracle.f16_to_f32(h).reshape(-1), k)
+    torch.cuda.synchronize()
+    _check(swa.avg, means, "swa f16")
 
 
 @pytest.mark.parametrize("layout", ["dense", "ld_pad", "misaligned"])

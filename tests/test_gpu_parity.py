@@ -20,7 +20,7 @@ if not torch.cuda.is_available():
 import oracle  # noqa: E402
 import synth  # noqa: E402
 from int6_weight_export_amd import ops, pgq  # noqa: E402
-from tests.gpu_util import bf16_dev, dev, f32, f32_bits_equal, same_bits, u16  # noqa: E402
+from tests.gpu_util import bf16_dev, dev, f16_dev, f32, f32_bits_equal, same_bits, u16  # noqa: E402
 
 
 def say(msg):
@@ -120,6 +120,59 @@ def test_export_bf16_flat_runs(q):
         assert o["kind"] == r["kind"], (nm, o["kind"], r["kind"])
         same_bits(o["codes"].cpu().numpy(), r["codes"], nm + " codes")
         same_bits(u16(o["scales"]), r["scales"], nm + " scales")
+        f32_bits_equal(f32(o["dq"]).reshape(-1), r["dq"].reshape(-1), nm + " dq")
+
+
+def _f16_weights(rng, shape, scale=0.02):
+    """fp16 bit patterns of N(0, scale^2) weights with a few edge values: fp16 subnormals, a large
+    magnitude and a signed zero."""
+    w = (rng.standard_normal(shape) * scale).astype(np.float32)
+    flat = w.reshape(-1)
+    k = flat.size
+    flat[: min(4, k)] = np.float32([3e-7, -5e-8, -0.0, 0.0])[: min(4, k)]
+    if k > 9:
+        flat[9] = np.float32(-7.25)
+    return oracle.f32_to_f16(w)
+
+
+@pytest.mark.parametrize("rows,cols", [(5, 528), (3, 100), (4, 1584), (2, 4100), (7, 8)])
+def test_f16_input_rows(rows, cols):
+    """fp16 weights (widened exactly to binary32): vector, element-wise and streamed rows, absmax and
+    a percentile clip, fp32 and bf16 dequant."""
+    say(f"fp16 input {rows}x{cols}")
+    h = _f16_weights(np.random.default_rng(cols + 1), (rows, cols))
+    w32 = oracle.f16_to_f32(h)
+    for pct in [(1, 1), (99, 100)]:
+        out = ops.quantize_rows(f16_dev(h), bits=6, pct=pct)
+        torch.cuda.synchronize()
+        _check_rows(w32, out, 31, pct[0], pct[1], f"f16 {rows}x{cols} {pct}")
+    out = ops.quantize_rows(f16_dev(h), bits=8, dq_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _check_rows(w32, out, 127, 1, 1, f"f16 {rows}x{cols} int8 bf16 dq", dq_bf16=True)
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_f16_input_export_model(per_tensor):
+    """The 9-layer set as fp16 weights: int6 99.99th-percentile rows (or per-tensor clips), int8
+    tok_emb, fp16 passthrough of the vectors (an identity on fp16 input), fp32 dequant."""
+    say(f"fp16 9-layer export, per_tensor={per_tensor}")
+    named = [(t.name, oracle.f32_to_f16(t.data)) for t in synth.config2()]
+    ex = ops.Exporter([ops.ExportTensor(nm, f16_dev(h)) for nm, h in named],
+                      ops.make_policy(per_tensor=per_tensor), want_dq=True)
+    ex.run()
+    ex.run()
+    torch.cuda.synchronize()
+    assert int(ex.status.item()) == 0
+    outs = ex.outputs()
+    ref = oracle.export([(nm, oracle.f16_to_f32(h)) for nm, h in named], oracle.Policy(per_tensor=per_tensor))
+    for o, r, (nm, h) in zip(outs, ref, named):
+        assert o["kind"] == r["kind"], (nm, o["kind"], r["kind"])
+        if r["kind"] == oracle.KIND_F16:
+            same_bits(u16(o["f16"]).reshape(-1), r["f16"].reshape(-1), nm + " f16")
+            same_bits(u16(o["f16"]).reshape(-1), np.asarray(h).reshape(-1), nm + " f16 identity")
+        else:
+            same_bits(o["codes"].cpu().numpy().reshape(r["codes"].shape), r["codes"], nm + " codes")
+            same_bits(u16(o["scales"]), r["scales"], nm + " scales")
         f32_bits_equal(f32(o["dq"]).reshape(-1), r["dq"].reshape(-1), nm + " dq")
 
 
