@@ -70,7 +70,7 @@ struct alignas(64) TState {
 };
 
 struct alignas(16) Desc {
-    const void* w;            // input rows (fp32 or bf16), row stride ld elements
+    const void* w;            // input rows (fp32, bf16 or fp16), row stride ld elements
     int8_t* codes;            // rows x cols, dense
     uint16_t* scales;         // rows fp16
     void* dq;                 // rows x cols dense: fp32 or bf16 (dq_dtype)

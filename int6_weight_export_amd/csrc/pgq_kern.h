@@ -4,12 +4,17 @@
 // kernels of some modes, so that the library's many instantiations compile in parallel.
 //
 // Design (HBM-streaming, no dense contraction, so no MFMA):
-//   * one 64-lane wavefront owns one row; a row of up to 2048 fp32 / 2048 bf16 values is
-//     loaded once with 16-byte loads (global_load_dwordx4) and stays in VGPRs while its
-//     clip is found, then every output is written once with coalesced stores;
-//   * the clip is a wave-wide max (k = n), an iterated wave max for ranks near the top,
-//     or an LDS-histogram radix select over the 31-bit magnitude patterns (8, 8, 8, 7
-//     bits), exact for any k;
+//   * one 64-lane wavefront owns a group of rows; a row of up to 2048 values is loaded once
+//     with 16-byte loads (fp32 x4; bf16 / fp16 x8, bf16 kept packed two per register) and
+//     stays in VGPRs while its clip is found, then every output is written once with
+//     coalesced non-temporal stores;
+//   * dense bf16 rows whose width leaves a partly used wave-wide load per row are read several
+//     rows at a time as one contiguous run (flat runs), so only the run's last load is partial;
+//   * the clip is a wave-wide max (k = n), an iterated wave max for ranks near the top, a
+//     candidate select, or an LDS-histogram radix select over the 31-bit magnitude patterns
+//     (8, 8, 8, 7 bits), exact for any k; a whole-tensor clip comes from one read of the tensor
+//     (every workgroup keeps the keys that can still be it, one workgroup per tensor ranks them)
+//     or from radix passes;
 //   * a grouped launch gives every tile of rows (of any tensor) its own workgroup, so a
 //     whole model (many tensors of different widths) is one launch;
 //   * longer rows stream through the same code in register-sized pieces, re-reading the
