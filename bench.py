@@ -43,14 +43,23 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0          # dense bf16 matrix-core peak of the MI3
 RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # 312.5
 KERNEL_SOURCES = sorted(os.path.relpath(p, ROOT) for p in glob.glob(os.path.join(ROOT, "int6_weight_export_amd", "csrc", "*"))
                         if p.endswith((".hip", ".h")))
+GEMM_SOURCE = os.path.join("int6_weight_export_amd", "csrc", "pgq_gemm.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 HOST_WORKERS = 16                       # host threads for input generation and the CPU leg
 CONFIG_MODES = ("batch", "fakequant", "awq", "sqwa")   # timed beside the export in the default run
 
 
-def kernel_source_hash() -> str:
+def kernel_sources(mode: str) -> list:
+    """The sources a mode's kernels are built from: the GEMM file for qgemm, every other kernel
+    source for the rest (the host API, the shared descriptor and the header for both)."""
+    if mode == "qgemm":
+        return [f for f in KERNEL_SOURCES if f == GEMM_SOURCE or f.endswith(("pgq_api.hip", "pgq_desc.h"))]
+    return [f for f in KERNEL_SOURCES if f != GEMM_SOURCE]
+
+
+def kernel_source_hash(mode: str = "export") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources(mode):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -65,7 +74,7 @@ def traffic_for(mode: str):
         return None
     with open(path) as f:
         tr = json.load(f)
-    if tr.get("kernel_source_sha256") != kernel_source_hash():
+    if tr.get("kernel_source_sha256") != kernel_source_hash(mode):
         return None
     return tr.get("hbm_bytes_per_step")
 
@@ -146,7 +155,8 @@ def profile_summary(d: str) -> None:
     hbm = res["FETCH_SIZE"]["per_step"] + res["WRITE_SIZE"]["per_step"]
     out = {
         "mode": mode, "workload": tl["config"]["workload"], "dominant_kernel": dom,
-        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_source_sha256": kernel_source_hash(mode),
+        "kernel_sources": kernel_sources(mode),
         "kernels": kern,
         "kernel_us_per_step": round(step_us, 3),
         "hbm_read_bytes_per_step": round(res["FETCH_SIZE"]["per_step"]),
@@ -180,7 +190,8 @@ def profile_summary(d: str) -> None:
     md += ["", f"Kernel time per step {step_us:.3f} us.  HBM traffic per step {round(hbm):,} B "
            f"(read {round(res['FETCH_SIZE']['per_step']):,}, written {round(res['WRITE_SIZE']['per_step']):,}) "
            f"against {alg:,} algorithmic bytes: ratio {hbm / alg:.4f}.", "",
-           f"Kernel sources sha256: `{kernel_source_hash()}`.", ""]
+           f"Kernel sources ({', '.join(os.path.basename(f) for f in kernel_sources(mode))}) sha256: "
+           f"`{kernel_source_hash(mode)}`.", ""]
     with open(os.path.join(PROFILES, f"{mode}_kernel_trace.md"), "w") as f:
         f.write("\n".join(md))
     print(json.dumps({"mode": mode, "kernel_us_per_step": round(step_us, 3), "traffic_over_algorithmic": round(hbm / alg, 4)}))

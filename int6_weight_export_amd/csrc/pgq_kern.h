@@ -44,6 +44,9 @@ namespace {
 constexpr int kFastRank = 8;     // ranks up to this use the iterated wave max
 
 #define GLB __attribute__((address_space(1)))
+// lambdas of the row paths are inlined like the __forceinline__ functions around them (a call
+// would put the row's registers on the stack)
+#define PGQ_AI __attribute__((always_inline))
 
 // Pointers taken from descriptors are generic; the data all live in global memory, so cast
 // them once per row (uniform, scalar registers) and address lanes with 32-bit offsets.
@@ -357,13 +360,13 @@ __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t
         // iterated maximum: strip the largest distinct magnitudes until r elements are covered.
         // One pass per round: the count of the current maximum m and the largest key below it.
         uint32_t m = 0;
-        each([&](uint32_t k, bool ok) { if (ok) m = max(m, k); });
+        each([&](uint32_t k, bool ok) PGQ_AI { if (ok) m = max(m, k); });
         m = wave_max(m);
         uint32_t rem = (uint32_t)r;
         // each round removes at least one element, so r rounds always suffice
         for (int round = 0; round < kFastRank && rem > 1; ++round) {
             uint32_t c = 0, below = 0;
-            each([&](uint32_t k, bool ok) {
+            each([&](uint32_t k, bool ok) PGQ_AI {
                 c += (ok && k == m) ? 1u : 0u;
                 if (ok && k < m) below = max(below, k);
             });
@@ -380,14 +383,14 @@ __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t
         // elements >= t0.  When there are at most 64 of them (the usual case for r <= 64 unless
         // many keys tie), they are packed one per lane through LDS and ranked directly.
         uint32_t lm = 0;                       // a lane with no element offers 0 (<= every key)
-        each([&](uint32_t k, bool ok) { if (ok) lm = max(lm, k); });
+        each([&](uint32_t k, bool ok) PGQ_AI { if (ok) lm = max(lm, k); });
         const uint32_t t0 = rank_select64(lm, (uint32_t)r);
         uint32_t c = 0;
-        each([&](uint32_t k, bool ok) { c += (ok && k >= t0) ? 1u : 0u; });
+        each([&](uint32_t k, bool ok) PGQ_AI { c += (ok && k >= t0) ? 1u : 0u; });
         c = wave_sum(c);
         if (c <= 64) {
             uint32_t base = 0;                 // uniform: candidates already packed
-            each([&](uint32_t k, bool ok) {
+            each([&](uint32_t k, bool ok) PGQ_AI {
                 const bool cand = ok && k >= t0;
                 const uint64_t b = __ballot(cand);
                 const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
@@ -410,7 +413,7 @@ __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t
         const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
         for (int b = lane; b < 256; b += 64) hist[b] = 0;
         lds_sync_wave();
-        each([&](uint32_t k, bool ok) {
+        each([&](uint32_t k, bool ok) PGQ_AI {
             if (ok && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xFFu], 1u);
         });
         lds_sync_wave();
@@ -887,7 +890,7 @@ __device__ __forceinline__ void quant_rows(const Desc& d, int64_t row0, int nrow
                 ck = mx;
                 if constexpr (SEL) {
                     if (d.rank_top > 1) {
-                        auto each = [&](auto&& f) {
+                        auto each = [&](auto&& f) PGQ_AI {
 #pragma unroll
                             for (int i = 0; i < NCH; ++i)
                                 if (EXACT || 64 * i < nchunk)
@@ -953,7 +956,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         const GLB void* wrow = (const GLB uint8_t*)gp(d.w) + (size_t)(row * d.ld) * esz;
         const RowOut ro = row_out(d, row);
         // cu: uniform chunk base of the piece; lane l takes chunk cu + l
-        auto load_chunk = [&](uint32_t cu, XC& x, float (&a)[VEC], float (&ainv)[VEC], GLB uint16_t* aw) {
+        auto load_chunk = [&](uint32_t cu, XC& x, float (&a)[VEC], float (&ainv)[VEC], GLB uint16_t* aw) PGQ_AI {
             x.load(offset_row<IN>(wrow, cu * VEC), (uint32_t)lane * VEC);
             if constexpr (!RAW) {
                 if (has_awq) {
@@ -987,7 +990,7 @@ __device__ __forceinline__ void rows_quant(const Desc& d, int64_t row0, int nrow
         if constexpr (SEL) {
             if (!tensor && d.rank_top > 1) {
                 // f runs in uniform control flow (lanes past the row pass ok = false)
-                auto each = [&](auto&& f) {
+                auto each = [&](auto&& f) PGQ_AI {
                     for (int base = 0; base < nchunk; base += 64) {
                         const bool ok = base + lane < nchunk;
                         XC x;
@@ -1149,8 +1152,8 @@ __device__ __forceinline__ void rows_flat(const Desc& d, const Groups& gs, int l
 {
     using Regs = FlatRegs<MODE, IT>;
     over_groups<Regs>(
-        gs, [&](Regs& g, int k) { load_flat<MODE, IT>(d, gs.row(k), gs.n(k), lane, ka, g); },
-        [&](Regs& g, int k) { quant_flat<MODE, IT>(d, gs.row(k), gs.n(k), lane, tab, ka, st, g); });
+        gs, [&](Regs& g, int k) PGQ_AI { load_flat<MODE, IT>(d, gs.row(k), gs.n(k), lane, ka, g); },
+        [&](Regs& g, int k) PGQ_AI { quant_flat<MODE, IT>(d, gs.row(k), gs.n(k), lane, tab, ka, st, g); });
 }
 
 // Run rows_quant with the group shape the host chose for this tensor.  Vector paths use the
@@ -1161,8 +1164,8 @@ __device__ __forceinline__ void rows_exact(const Desc& d, const Groups& gs, int 
 {
     using Regs = RowsRegs<MODE, AWQ, IN, VEC, R, NCH>;
     over_groups<Regs>(
-        gs, [&](Regs& g, int k) { load_rows<MODE, AWQ, IN, VEC, R, NCH, true>(d, gs.row(k), gs.n(k), lane, ka, g); },
-        [&](Regs& g, int k) {
+        gs, [&](Regs& g, int k) PGQ_AI { load_rows<MODE, AWQ, IN, VEC, R, NCH, true>(d, gs.row(k), gs.n(k), lane, ka, g); },
+        [&](Regs& g, int k) PGQ_AI {
             quant_rows<MODE, AWQ, SEL, IN, VEC, R, NCH, true>(d, gs.row(k), gs.n(k), lane, hist, awq_lds, ka, st, g);
         });
 }
@@ -1457,7 +1460,7 @@ template <uint32_t F, class Fn>
 __device__ __forceinline__ void with_input(const Desc& d, Fn&& f)
 {
     const bool vec = (d.flags & DF_VEC) != 0;
-    auto pick = [&](auto in) {
+    auto pick = [&](auto in) PGQ_AI {
         constexpr int IN = decltype(in)::IN;
         if constexpr ((F & F_SCALAR) != 0) {
             if (!vec) { f(In<IN, 1>()); return; }
@@ -1483,7 +1486,7 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, const Groups& gs, i
     constexpr bool SCALAR = (F & F_SCALAR) != 0;
     const bool vec = (d.flags & DF_VEC) != 0;
     // f(row) for every row of the wave's groups (row-wise paths)
-    auto each_row = [&](auto&& f) {
+    auto each_row = [&](auto&& f) PGQ_AI {
         for (int g = 0; g < gs.count; ++g) {
             const int nrows = gs.n(g);
             if (nrows <= 0) break;
@@ -1491,14 +1494,14 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, const Groups& gs, i
         }
     };
     if constexpr (MODE == MODE_DECODE) {
-        each_row([&](int64_t row) { row_decode(d, row, lane); });
+        each_row([&](int64_t row) PGQ_AI { row_decode(d, row, lane); });
     } else if constexpr (MODE == MODE_EMA || MODE == MODE_SWA) {
-        with_input<F>(d, [&](auto in) {
+        with_input<F>(d, [&](auto in) PGQ_AI {
             using I = decltype(in);
-            each_row([&](int64_t row) { row_average<MODE, I::IN, I::VEC>(d, row, lane, ka, st); });
+            each_row([&](int64_t row) PGQ_AI { row_average<MODE, I::IN, I::VEC>(d, row, lane, ka, st); });
         });
     } else if constexpr (MODE == MODE_FQ_BWD) {
-        each_row([&](int64_t row) {
+        each_row([&](int64_t row) PGQ_AI {
             if (vec) row_fq_bwd<8>(d, row, lane);
             else row_fq_bwd<1>(d, row, lane);
         });
@@ -1511,14 +1514,14 @@ __device__ __forceinline__ void dispatch_rows(const Desc& d, const Groups& gs, i
     } else {
         if constexpr ((F & F_PASS) != 0) {
             if (d.kind == KIND_F16) {
-                with_input<F>(d, [&](auto in) {
+                with_input<F>(d, [&](auto in) PGQ_AI {
                     using I = decltype(in);
-                    each_row([&](int64_t row) { row_passthrough<MODE, I::IN, I::VEC>(d, row, lane, ka, st); });
+                    each_row([&](int64_t row) PGQ_AI { row_passthrough<MODE, I::IN, I::VEC>(d, row, lane, ka, st); });
                 });
                 return;
             }
         }
-        with_input<F>(d, [&](auto in) {
+        with_input<F>(d, [&](auto in) PGQ_AI {
             using I = decltype(in);
             rows_quant_r<MODE, AWQ, SEL, LONG, I::IN, I::VEC>(d, gs, lane, hist, awq_lds, ka, st);
         });
@@ -1809,7 +1812,7 @@ __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, i
 {
     if constexpr (MODE == MODE_TCAND) {
         uint32_t* wl = hist - 256 * wave;           // the workgroup's 4 x 256 words of LDS
-        with_input<F>(d, [&](auto in) {
+        with_input<F>(d, [&](auto in) PGQ_AI {
             using I = decltype(in);
             tile_tensor_cand<I::IN, I::VEC>(d, row0, wave, lane, wl, st);
         });
@@ -1818,7 +1821,7 @@ __device__ __forceinline__ void do_tile(const Desc& d, int64_t row0, int wave, i
     if constexpr (MODE == MODE_TSEL) {
         uint32_t* wg_hist = hist - 256 * wave;      // the workgroup's LDS histograms, 4 x 256 words
         const int64_t nrows = (int64_t)d.tile_rows * ka.tsel_group;   // row0 counts select tiles
-        with_input<F>(d, [&](auto in) {
+        with_input<F>(d, [&](auto in) PGQ_AI {
             using I = decltype(in);
             tile_tensor_select<I::IN, I::VEC>(d, row0, nrows, wave, lane, wg_hist, ka, st);
         });

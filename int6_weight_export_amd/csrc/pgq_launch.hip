@@ -49,7 +49,7 @@ __device__ void cand_pick(const Desc* dp, GLB TState* S, uint32_t* sl, uint32_t*
         }
     }
     // every valid candidate: from the registers, or streamed in four-slot groups
-    auto each = [&](auto&& f) {
+    auto each = [&](auto&& f) PGQ_AI {
         if (held) {
 #pragma unroll
             for (int g = 0; g < kPickGroups; ++g)
@@ -70,11 +70,11 @@ __device__ void cand_pick(const Desc* dp, GLB TState* S, uint32_t* sl, uint32_t*
         }
     };
     uint32_t lm = 0;
-    each([&](uint32_t k) { lm = max(lm, k + 1u); });
+    each([&](uint32_t k) PGQ_AI { lm = max(lm, k + 1u); });
     const uint32_t t1 = wg_lower_bound<kPickWaves>(lm, R, wave, lane, sl);
     if (tid == 0) sl[300] = 0;
     __syncthreads();
-    each([&](uint32_t k) {
+    each([&](uint32_t k) PGQ_AI {
         if (k + 1u >= t1) {
             const uint32_t slot = atomicAdd(&sl[300], 1u);
             if (slot < kPickBuf) buf[slot] = k;
@@ -100,7 +100,7 @@ __device__ void cand_pick(const Desc* dp, GLB TState* S, uint32_t* sl, uint32_t*
         const int shift = pass == 0 ? 23 : pass == 1 ? 15 : pass == 2 ? 7 : 0;
         if (tid < 256) buf[tid] = 0;
         __syncthreads();
-        each([&](uint32_t k) {
+        each([&](uint32_t k) PGQ_AI {
             if ((k & pmask) == prefix) atomicAdd(&buf[(k >> shift) & 0xFFu], 1u);
         });
         __syncthreads();
