@@ -14,7 +14,9 @@ fp32 instructions disabled.
 from __future__ import annotations
 
 import glob
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -50,16 +52,44 @@ def _jobs() -> int:
     return max(1, min(n, 16, len(SOURCES)))
 
 
+RESOURCES = os.path.join(OBJ_DIR, "resources.json")
+_FIELDS = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy",
+           "VGPRs Spill": "vgpr_spill", "SGPRs Spill": "sgpr_spill"}
+
+
+def _resources(remarks: str) -> dict:
+    """Per-kernel register, scratch and occupancy figures from the compiler's resource-usage
+    remarks (-Rpass-analysis=kernel-resource-usage)."""
+    out, name = {}, None
+    for ln in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", ln)
+        if m:
+            name = m.group(1)
+            out[name] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][^:]*): (\d+) \[-Rpass-analysis", ln)
+        if m and name and m.group(1) in _FIELDS:
+            out[name][_FIELDS[m.group(1)]] = int(m.group(2))
+    return out
+
+
 def _compile(src: str, incremental: bool, verbose: bool) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
-    if incremental and os.path.exists(obj):
+    res = obj[:-2] + ".resources.json"
+    if incremental and os.path.exists(obj) and os.path.exists(res):
         newest = max(os.path.getmtime(p) for p in [src, *HEADERS, __file__])
         if os.path.getmtime(obj) > newest:
             return obj
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj + ".tmp", src]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-I", os.path.join(ROOT, "include"), "-c",
+           "-o", obj + ".tmp", src]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+    with open(res, "w") as f:
+        json.dump(_resources(r.stderr), f, indent=0)
     os.replace(obj + ".tmp", obj)
     return obj
 
@@ -68,6 +98,12 @@ def build_library(verbose: bool = False, incremental: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     with ThreadPoolExecutor(_jobs()) as pool:
         objs = list(pool.map(lambda s: _compile(s, incremental, verbose), SOURCES))
+    merged = {}
+    for o in objs:
+        with open(o[:-2] + ".resources.json") as f:
+            merged.update(json.load(f))
+    with open(RESOURCES, "w") as f:
+        json.dump(merged, f, indent=0)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
