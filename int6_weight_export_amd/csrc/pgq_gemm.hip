@@ -297,9 +297,21 @@ pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t l
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // one 32-wide K block of the stage at la / lb: 16 MFMAs per wavefront
+    // one 32-wide K block of the stage at la / lb: 16 MFMAs per wavefront.  Every fragment is read
+    // first and the MFMAs go over all eight accumulators before one is used again (2-3% faster
+    // than reading the X fragments block row by block row).
     auto block = [&](const uint8_t* la, const uint8_t* lb, int kb) {
+        bf16x8 fa[kIB][2];                               // [i][t]
         bf16x8 fb[2][2];                                 // [j][t]
+#pragma unroll
+        for (int i = 0; i < kIB; ++i) {
+            const int r = wm + 32 * i + r32;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int g = 4 * kb + 2 * h + t;
+                fa[i][t] = *reinterpret_cast<const bf16x8*>(la + (r * 8 + (g ^ swz_a(r))) * 16);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int r = wn + 32 * j + r32;
@@ -308,20 +320,12 @@ pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t l
             codes_to_bf16(q, sc[j], sc128[j], fb[j][0], fb[j][1]);
         }
 #pragma unroll
-        for (int i = 0; i < kIB; ++i) {
-            const int r = wm + 32 * i + r32;
-            bf16x8 fa[2];
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int g = 4 * kb + 2 * h + t;
-                fa[t] = *reinterpret_cast<const bf16x8*>(la + (r * 8 + (g ^ swz_a(r))) * 16);
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < kIB; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t], fb[j][t], acc[i][j], 0, 0, 0);
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][t], fb[j][t], acc[i][j], 0, 0, 0);
     };
     // stage st: wait for its loads, then the barrier after which every wave's loads of st are in
     // LDS and every wave is done reading the other buffer, which the next stage's loads then fill
