@@ -251,6 +251,10 @@ void set_grouping(Desc& d, int mode)
             }
         }
     }
+    // decode rows are short (a few KB of output each): two rows per wavefront halve the tiles and
+    // their per-workgroup start-up (measured 23.2 -> 20.0 us on the 9-layer artifact); four or
+    // eight rows per wavefront, one after another, ran slower
+    if (mode == MODE_DECODE) R = 2;
     d.rgroup = R;
     const bool awq_tile = d.awq_s && d.kind != KIND_F16 && mode != MODE_FQ && mode != MODE_FQ_BWD;
     d.tile_rows = kWaves * R * std::max(kGroupsPerWave, awq_tile ? kAwqGroupsPerWave : 1);
