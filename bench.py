@@ -52,7 +52,7 @@ CONFIG_MODES = ("batch", "fakequant", "awq", "sqwa")   # timed beside the export
 def kernel_sources(mode: str) -> list:
     """The sources a mode's kernels are built from: the GEMM file for qgemm, every other kernel
     source for the rest (the host API, the shared descriptor and the header for both)."""
-    if mode == "qgemm":
+    if mode in ("qgemm", "qgemm16"):
         return [f for f in KERNEL_SOURCES if f == GEMM_SOURCE or f.endswith(("pgq_api.hip", "pgq_desc.h"))]
     return [f for f in KERNEL_SOURCES if f != GEMM_SOURCE]
 
@@ -488,10 +488,11 @@ def workload_decode(copies, torch, ops):
                     lambda: [int(s[0].status.item()) for s in sets], cfg, "pgq_table_kernel<8, 1u>", copies=copies)
 
 
-def workload_qgemm(copies, torch, ops):
+def _workload_qgemm(copies, torch, ops, ybf16):
     """The QAT forward's consumer GEMM with the STE dequantization fused in: 16384 tokens through
     the d=528 unified Q/K/V projection (What 1584 x 528 from int8 codes + fp16 row scales, both
-    from the library's own fake-quant forward), bf16 MFMA with fp32 accumulation."""
+    from the library's own fake-quant forward), bf16 MFMA with fp32 accumulation; Y fp32, or bf16
+    (the QAT forward's activation type) with ybf16."""
     from int6_weight_export_amd import pgq
 
     M, N, K = 16384, 1584, 528
@@ -500,18 +501,32 @@ def workload_qgemm(copies, torch, ops):
     fq = ops.FakeQuant([w], want_codes=True)
     fq.run(pgq.PGQ_FQ_FWD)
     codes, scales = fq.codes[0], fq.scales[0]
+    ydt = torch.bfloat16 if ybf16 else torch.float32
     sets = []
     for k in range(copies):
         gk = torch.Generator(device="cuda").manual_seed(1 + k)
         x = torch.randn(M, K, generator=gk, device="cuda").to(torch.bfloat16)
-        sets.append((x, torch.empty(M, N, dtype=torch.float32, device="cuda")))
-    nbytes = 2 * M * K + N * K + 2 * N + 4 * M * N
+        sets.append((x, torch.empty(M, N, dtype=ydt, device="cuda")))
+    ysz = 2 if ybf16 else 4
+    nbytes = 2 * M * K + N * K + 2 * N + ysz * M * N
     cfg = {"workload": "fused-dequant GEMM of the QAT forward: Y[16384 x 1584] = X[16384 x 528] (bf16) times "
-                       "bf16(code * s)^T from int8 codes and fp16 row scales, fp32 accumulation on MFMA, fp32 Y",
+                       "bf16(code * s)^T from int8 codes and fp16 row scales, fp32 accumulation on MFMA, "
+                       + ("bf16 Y (round to nearest even of the fp32 result)" if ybf16 else "fp32 Y"),
            "M": M, "N": N, "K": K}
-    return Workload("qgemm", nbytes, M,
-                    lambda i: ops.qgemm(sets[i % len(sets)][0], codes, scales, out=sets[i % len(sets)][1]),
-                    lambda: [int(fq.status.item())], cfg, "pgq_qgemm_kernel", flops=2 * M * N * K, copies=copies)
+    return Workload("qgemm16" if ybf16 else "qgemm", nbytes, M,
+                    lambda i: ops.qgemm(sets[i % len(sets)][0], codes, scales, out=sets[i % len(sets)][1],
+                                        out_dtype=ydt),
+                    lambda: [int(fq.status.item())], cfg,
+                    "pgq_qgemm_kernel<unsigned short>" if ybf16 else "pgq_qgemm_kernel<float>",
+                    flops=2 * M * N * K, copies=copies)
+
+
+def workload_qgemm(copies, torch, ops):
+    return _workload_qgemm(copies, torch, ops, False)
+
+
+def workload_qgemm16(copies, torch, ops):
+    return _workload_qgemm(copies, torch, ops, True)
 
 
 def _workload_average(kind, copies, torch, ops):
@@ -554,7 +569,8 @@ def workload_swa(copies, torch, ops):
 
 MAKERS = {"export": workload_export, "awq": workload_awq, "batch": workload_batch, "select": workload_select,
           "fakequant": workload_fakequant, "sqwa": workload_sqwa, "ema": workload_ema, "swa": workload_swa,
-          "tensor": workload_tensor, "pack6": workload_pack6, "decode": workload_decode, "qgemm": workload_qgemm}
+          "tensor": workload_tensor, "pack6": workload_pack6, "decode": workload_decode, "qgemm": workload_qgemm,
+          "qgemm16": workload_qgemm16}
 DEFAULT_STEPS = {"sqwa": 50}
 DEFAULT_WARMUP = {"sqwa": 3}
 CONFIG_STEPS = {"batch": 50, "fakequant": 100, "awq": 100, "sqwa": 5}     # steps of each `configs` entry
@@ -696,7 +712,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.mode in ("fakequant", "qgemm") else "f32",
+        "dtype": "bf16" if args.mode in ("fakequant", "qgemm", "qgemm16") else "f32",
         "data": "synthetic",
         "config": config,
         "roofline": roofline(wl, m),

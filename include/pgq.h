@@ -281,6 +281,14 @@ pgq_status pgq_dequant_model(const pgq_tensor_in* t, int32_t n, const pgq_tensor
 pgq_status pgq_qgemm_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
                           const uint16_t* scales, int64_t N, float* y, int64_t ldy, void* stream);
 
+/* The same GEMM with Y stored as bf16: the QAT forward's activations are bf16 (same card and    */
+/* section).  Every element is bf16 (round to nearest even) of the fp32 value pgq_qgemm_bf16    */
+/* writes for the same inputs, bit for bit: the accumulation is shared, only the store differs. */
+/*   y       device bf16 bit patterns, M x N, row stride ldy >= N (written, not accumulated)    */
+/* Other arguments, limits and errors as for pgq_qgemm_bf16; y must be 2-byte aligned.         */
+pgq_status pgq_qgemm_bf16_ybf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes,
+                                int64_t ldc, const uint16_t* scales, int64_t N, uint16_t* y, int64_t ldy, void* stream);
+
 /* ------------------------------------------------------------------------------------------ */
 /* Weight averaging without quantization, grouped over n tensors in one launch.               */
 /* w[i]: the weights (fp32 or bf16, rows x cols, row stride ld; awq_s must be NULL; name is    */

@@ -621,6 +621,25 @@ pgq_status export_descs(const pgq_tensor_in* t, int32_t n, const pgq_tensor_plan
 
 }  // namespace
 
+// The checks and launch of both GEMM entry points; esz = bytes of a Y element (4 or 2).
+static pgq_status qgemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
+                        const uint16_t* scales, int64_t N, void* y, int64_t ldy, int esz, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || ldx < K || ldc < K || ldy < N) return PGQ_ERR_SHAPE;
+    if (M > (int64_t)65535 * 128 || N > ((int64_t)1 << 31) || K > ((int64_t)1 << 31)) return PGQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return PGQ_OK;
+    if (!y || (K > 0 && (!x || !codes || !scales))) return PGQ_ERR_NULL;
+    if ((x && !aligned(x, 2)) || (scales && !aligned(scales, 2)) || !aligned(y, esz)) return PGQ_ERR_ALIGN;
+    uint32_t f = 0;
+    if (x && ldx % 8 == 0 && aligned(x, 16)) f |= 1u;
+    if (codes && ldc % 16 == 0 && aligned(codes, 16)) f |= 2u;
+    if (ldy % (16 / esz) == 0 && aligned(y, 16)) f |= 4u;
+    if (const int e = launch_qgemm(x, M, K, ldx, codes, ldc, scales, N, y, ldy, esz == 2, f, stream))
+        return hip_failed((hipError_t)e);
+    if (const hipError_t e = hipGetLastError()) return hip_failed(e);
+    return PGQ_OK;
+}
+
 extern "C" {
 
 const char* pgq_version(void) { return "pgq 0.1 (gfx950)"; }
@@ -868,18 +887,13 @@ pgq_status pgq_sqwa_accumulate(const pgq_tensor_in* snap, int32_t n, const pgq_t
 pgq_status pgq_qgemm_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
                           const uint16_t* scales, int64_t N, float* y, int64_t ldy, void* stream)
 {
-    if (M < 0 || N < 0 || K < 0 || ldx < K || ldc < K || ldy < N) return PGQ_ERR_SHAPE;
-    if (M > (int64_t)65535 * 128 || N > ((int64_t)1 << 31) || K > ((int64_t)1 << 31)) return PGQ_ERR_SHAPE;
-    if (M == 0 || N == 0) return PGQ_OK;
-    if (!y || (K > 0 && (!x || !codes || !scales))) return PGQ_ERR_NULL;
-    if ((x && !aligned(x, 2)) || (scales && !aligned(scales, 2)) || !aligned(y, 4)) return PGQ_ERR_ALIGN;
-    uint32_t f = 0;
-    if (x && ldx % 8 == 0 && aligned(x, 16)) f |= 1u;
-    if (codes && ldc % 16 == 0 && aligned(codes, 16)) f |= 2u;
-    if (ldy % 4 == 0 && aligned(y, 16)) f |= 4u;
-    if (const int e = launch_qgemm(x, M, K, ldx, codes, ldc, scales, N, y, ldy, f, stream)) return hip_failed((hipError_t)e);
-    if (const hipError_t e = hipGetLastError()) return hip_failed(e);
-    return PGQ_OK;
+    return qgemm(x, M, K, ldx, codes, ldc, scales, N, y, ldy, 4, stream);
+}
+
+pgq_status pgq_qgemm_bf16_ybf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes,
+                                int64_t ldc, const uint16_t* scales, int64_t N, uint16_t* y, int64_t ldy, void* stream)
+{
+    return qgemm(x, M, K, ldx, codes, ldc, scales, N, y, ldy, 2, stream);
 }
 
 pgq_status pgq_dequant_codes(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,

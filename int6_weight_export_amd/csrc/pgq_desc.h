@@ -135,10 +135,10 @@ void set_timing_events(void* start, void* stop);
 void take_timing_events(void** start, void** stop);
 // Any kernel with a 3-D grid, taking a pending timing-event pair like the others.
 hipError_t launch_plain(const void* fn, dim3 grid, dim3 block, void** args, void* stream);
-// The fused-dequant GEMM (pgq_gemm.hip); flags: bit 0 X rows 16-byte loadable, bit 1 code rows,
-// bit 2 Y rows 16-byte aligned.
+// The fused-dequant GEMM (pgq_gemm.hip), Y fp32 or (ybf16) bf16; flags: bit 0 X rows 16-byte
+// loadable, bit 1 code rows, bit 2 Y rows 16-byte aligned.
 int launch_qgemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
-                 const uint16_t* scales, int64_t N, float* y, int64_t ldy, uint32_t flags, void* stream);
+                 const uint16_t* scales, int64_t N, void* y, int64_t ldy, bool ybf16, uint32_t flags, void* stream);
 // Decode of stored codes to fp32 (rows > 0, cols > 0).
 int launch_decode(const void* codes, int32_t packed, int64_t rows, int64_t cols, const uint16_t* scales,
                   int32_t per_tensor, const uint16_t* awq, float* out, void* stream);

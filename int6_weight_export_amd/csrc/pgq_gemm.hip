@@ -52,12 +52,21 @@ __device__ __forceinline__ uint16_t to_bf16(float f)
     return __builtin_bit_cast(uint16_t, (__bf16)f);     // round to nearest even
 }
 
+// Y element: fp32, or bf16 (round to nearest even of the fp32 result) as it leaves
+template <typename YT>
+__device__ __forceinline__ YT y_of(float v);
+template <>
+__device__ __forceinline__ float y_of<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t y_of<uint16_t>(float v) { return to_bf16(v); }
+
 // flags: bit 0 = X rows are 16-byte loadable (ldx % 8 == 0, X 16-byte aligned),
 //        bit 1 = code rows are 16-byte loadable (ldc % 16 == 0, codes 16-byte aligned)
+template <typename YT>
 __global__ void __launch_bounds__(256) pgq_qgemm_generic_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        int64_t ldx, const int8_t* __restrict__ codes, int64_t ldc,
                                                        const uint16_t* __restrict__ scales, int64_t N,
-                                                       float* __restrict__ y, int64_t ldy, uint32_t flags)
+                                                       YT* __restrict__ y, int64_t ldy, uint32_t flags)
 {
     __shared__ __align__(16) uint16_t As[kBM][kPad];
     __shared__ __align__(16) uint16_t Bs[kBN][kPad];
@@ -158,7 +167,7 @@ __global__ void __launch_bounds__(256) pgq_qgemm_generic_kernel(const uint16_t* 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < M && col < N) y[row * ldy + col] = acc[i][j][r];
+                if (row < M && col < N) y[row * ldy + col] = y_of<YT>(acc[i][j][r]);
             }
         }
 }
@@ -220,9 +229,11 @@ __device__ __forceinline__ void codes_to_bf16(u32x4 q, float s, float s128, bf16
 // (rows 128 (w / 2), columns 64 (w % 2)) as 4 x 2 blocks of 32 x 32.  Occupancy floor of two
 // wavefronts per SIMD (the register budget the 128 accumulators leave), matching the two
 // workgroups per compute unit that the 80 KB of LDS allow.
+template <typename YT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const int8_t* __restrict__ codes,
-                 int64_t ldc, const uint16_t* __restrict__ scales, int64_t N, float* __restrict__ y, int64_t ldy)
+                 int64_t ldc, const uint16_t* __restrict__ scales, int64_t N, YT* __restrict__ y, int64_t ldy,
+                 int32_t yvec)
 {
     __shared__ __align__(16) uint8_t lds[2 * (kAS + kBS)];
     const int tid = (int)threadIdx.x;
@@ -352,8 +363,10 @@ pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t l
     }
 
     // Y through an LDS transpose, one 32-row block at a time: 16-byte non-temporal stores of 4
-    // consecutive columns (one wavefront instruction covers 4 rows x 256 bytes).  Y is written once
-    // and never read here.  ldy % 4 == 0 and a 16-byte aligned Y are required (host-checked).
+    // consecutive fp32 columns (one wavefront instruction covers 4 rows x 256 bytes), or of 8
+    // consecutive bf16 columns (2 rows x 128 bytes), when yvec says that Y rows are 16-byte
+    // storable (a 16-byte aligned Y and ldy % 4 == 0 for fp32, ldy % 8 == 0 for bf16); element
+    // stores otherwise and at a ragged N edge.  Y is written once and never read here.
     float* tl = reinterpret_cast<float*>(lds) + wave * (32 * 68);   // rows padded to 68 floats
     lds_barrier();
 #pragma unroll
@@ -364,6 +377,31 @@ pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t l
             for (int r = 0; r < 16; ++r)
                 tl[(8 * (r >> 2) + 4 * h + (r & 3)) * 68 + 32 * j + r32] = acc[i][j][r];
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if constexpr (sizeof(YT) == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = lane + 64 * q;
+                const int rr = c >> 3, ch = c & 7;
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(tl + rr * 68 + 8 * ch);
+                const f32x4 v1 = *reinterpret_cast<const f32x4*>(tl + rr * 68 + 8 * ch + 4);
+                const int64_t row = m0 + wm + 32 * i + rr;
+                const int64_t col = n0 + wn + 8 * ch;
+                if (row < M) {
+                    GLB uint16_t* py = (GLB uint16_t*)y + row * ldy + col;
+                    if (yvec && col + 8 <= N) {
+                        const u32x4 w = {pk_bf16(v0[0], v0[1]), pk_bf16(v0[2], v0[3]), pk_bf16(v1[0], v1[1]),
+                                         pk_bf16(v1[2], v1[3])};
+                        __builtin_nontemporal_store(w, (GLB u32x4*)py);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (col + e < N) __builtin_nontemporal_store(to_bf16(e < 4 ? v0[e] : v1[e - 4]), py + e);
+                    }
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            continue;
+        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int c = lane + 64 * q;
@@ -373,7 +411,7 @@ pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t l
             const int64_t col = n0 + wn + 4 * ch;
             if (row < M) {
                 GLB float* py = (GLB float*)y + row * ldy + col;
-                if (col + 4 <= N) {
+                if (yvec && col + 4 <= N) {
                     __builtin_nontemporal_store(v, (GLB f32x4*)py);
                 } else {
 #pragma unroll
@@ -389,24 +427,28 @@ pgq_qgemm_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t l
 }  // namespace
 
 int launch_qgemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* codes, int64_t ldc,
-                 const uint16_t* scales, int64_t N, float* y, int64_t ldy, uint32_t flags, void* stream)
+                 const uint16_t* scales, int64_t N, void* y, int64_t ldy, bool ybf16, uint32_t flags, void* stream)
 {
-    // the main kernel: 16-byte loadable X and code rows and 16-byte aligned Y rows (flags bits 0..2),
-    // K a positive multiple of 16, and a tile's rows of either operand within a 31-bit buffer range
-    const bool main = (flags & 7u) == 7u && K > 0 && K % 16 == 0 && ldx < ((int64_t)1 << 21) &&
+    // the main kernel: 16-byte loadable X and code rows (flags bits 0, 1), K a positive multiple of
+    // 16, and a tile's rows of either operand within a 31-bit buffer range.  The choice does not
+    // depend on Y, so that both Y types accumulate alike; Y's 16-byte stores follow flags bit 2.
+    const bool main = (flags & 3u) == 3u && K > 0 && K % 16 == 0 && ldx < ((int64_t)1 << 21) &&
                       ldc < ((int64_t)1 << 23);
     if (main) {
         const uint64_t tiles = (uint64_t)((N + kTN - 1) / kTN) * (uint64_t)((M + kTM - 1) / kTM);
         if (tiles > 0xFFFFFFFFull) return (int)hipErrorInvalidValue;
-        void* args[] = {&x, &M, &K, &ldx, &codes, &ldc, &scales, &N, &y, &ldy};
-        return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_kernel), dim3((unsigned)tiles), dim3(256),
-                                 args, stream);
+        int32_t yvec = (flags & 4u) ? 1 : 0;
+        void* args[] = {&x, &M, &K, &ldx, &codes, &ldc, &scales, &N, &y, &ldy, &yvec};
+        const void* k = ybf16 ? reinterpret_cast<const void*>(&pgq_qgemm_kernel<uint16_t>)
+                              : reinterpret_cast<const void*>(&pgq_qgemm_kernel<float>);
+        return (int)launch_plain(k, dim3((unsigned)tiles), dim3(256), args, stream);
     }
     const uint64_t tiles = (uint64_t)((N + kBN - 1) / kBN) * (uint64_t)((M + kBM - 1) / kBM);
     if (tiles > 0xFFFFFFFFull) return (int)hipErrorInvalidValue;
     void* args[] = {&x, &M, &K, &ldx, &codes, &ldc, &scales, &N, &y, &ldy, &flags};
-    return (int)launch_plain(reinterpret_cast<const void*>(&pgq_qgemm_generic_kernel), dim3((unsigned)tiles),
-                             dim3(256), args, stream);
+    const void* k = ybf16 ? reinterpret_cast<const void*>(&pgq_qgemm_generic_kernel<uint16_t>)
+                          : reinterpret_cast<const void*>(&pgq_qgemm_generic_kernel<float>);
+    return (int)launch_plain(k, dim3((unsigned)tiles), dim3(256), args, stream);
 }
 
 }  // namespace pgq

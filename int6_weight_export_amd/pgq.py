@@ -98,6 +98,7 @@ SIGNATURES = {
                                    ctypes.POINTER(_P), _I32, _P, _SZ, _U32, _P, _P]),
     "pgq_dequant_codes": (_I32, [_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
     "pgq_qgemm_bf16": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
+    "pgq_qgemm_bf16_ybf16": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P]),
     "pgq_dequant_model": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(pgq_tensor_plan), _P,
                                  ctypes.POINTER(_P), _P, _SZ, _U32, _P, _P]),
     "pgq_average_workspace": (_I32, [ctypes.POINTER(pgq_tensor_in), _I32, ctypes.POINTER(_SZ)]),
@@ -169,6 +170,10 @@ def pgq_sqwa_accumulate(snap, n, plan, mean, k, workspace, workspace_bytes, flag
 
 def pgq_qgemm_bf16(x, M, K, ldx, codes, ldc, scales, N, y, ldy, stream):
     return _lib.pgq_qgemm_bf16(x, M, K, ldx, codes, ldc, scales, N, y, ldy, stream)
+
+
+def pgq_qgemm_bf16_ybf16(x, M, K, ldx, codes, ldc, scales, N, y, ldy, stream):
+    return _lib.pgq_qgemm_bf16_ybf16(x, M, K, ldx, codes, ldc, scales, N, y, ldy, stream)
 
 
 def pgq_dequant_codes(codes, packed, rows, cols, scales, per_tensor, awq_mult, out, dev_status, stream):

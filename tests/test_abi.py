@@ -334,8 +334,9 @@ def test_dequant_model_argument_errors():
     assert dm(arr, 4, plan, FAKE, outs, FAKE, wb.value, 0, None, None) == pgq.PGQ_ERR_PARAM
 
 
-def test_qgemm_argument_errors():
-    g = pgq.pgq_qgemm_bf16
+@pytest.mark.parametrize("entry,ysize", [("pgq_qgemm_bf16", 4), ("pgq_qgemm_bf16_ybf16", 2)])
+def test_qgemm_argument_errors(entry, ysize):
+    g = getattr(pgq, entry)
     # (x, M, K, ldx, codes, ldc, scales, N, y, ldy, stream)
     ok = dict(x=FAKE, M=4, K=32, ldx=32, codes=FAKE, ldc=32, scales=FAKE, N=8, y=FAKE, ldy=8)
 
@@ -358,7 +359,7 @@ def test_qgemm_argument_errors():
     assert call(scales=None) == pgq.PGQ_ERR_NULL
     assert call(x=FAKE + 1) == pgq.PGQ_ERR_ALIGN
     assert call(scales=FAKE + 1) == pgq.PGQ_ERR_ALIGN
-    assert call(y=FAKE + 2) == pgq.PGQ_ERR_ALIGN
+    assert call(y=FAKE + ysize // 2) == pgq.PGQ_ERR_ALIGN   # y must hold whole elements
 
 
 def test_per_tensor_export_without_weights_is_refused():

@@ -128,3 +128,76 @@ def test_qgemm_bench_shape_sampled_rows_and_repeatable():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     rows = np.r_[0:2, 126:131, 8000:8002, 16255:16258, 16382:16384]
     _check(a, x, codes, scales, rows=rows, what="bench shape")
+
+
+# ---- bf16 Y: each element is bf16 (round to nearest even) of the fp32 result of the same GEMM ----
+
+def _ybf16_tol(ref, bound, K):
+    """Against the exact product: the fp32 bound plus half a bf16 ulp of the value (bf16 keeps 8
+    significant bits, so half an ulp is at most 2^-8 |v|; 2^-133 covers the subnormal steps)."""
+    tol32 = (K + 1) * 2.0 ** -24 * bound
+    return tol32 + 2.0 ** -8 * (np.abs(ref) + tol32) + 2.0 ** -133
+
+
+def _bf16_bits_of(y32):
+    return oracle.f32_to_bf16(np.ascontiguousarray(y32, dtype=np.float32)).view(np.uint16)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (5, 7, 3), (129, 130, 33), (200, 1584, 528), (131, 257, 100),
+                                   (3, 5, 48), (130, 129, 64), (257, 300, 80), (384, 260, 176), (70, 13, 16)])
+def test_qgemm_ybf16_is_the_rounded_fp32_result(M, N, K):
+    say(f"qgemm bf16 Y {M}x{N}x{K}")
+    x, codes, scales = _inputs(M, N, K, 3 * M + N + K)
+    xd, cd, sd = _bf16(x), torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda()
+    y32 = ops.qgemm(xd, cd, sd)
+    y16 = ops.qgemm(xd, cd, sd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    a = y32.cpu().numpy()
+    b = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(b, _bf16_bits_of(a)), f"{M}x{N}x{K}: bf16 Y differs from bf16 of the fp32 Y"
+    ref, bound = oracle.qgemm_bf16(x, codes, scales)
+    got = oracle.bf16_to_f32(b).astype(np.float64)
+    err = np.abs(got - ref)
+    tol = _ybf16_tol(ref, bound, K)
+    assert np.all(err <= tol), f"{M}x{N}x{K}: max err {err.max()}"
+
+
+def test_qgemm_ybf16_strided_and_k_zero():
+    from int6_weight_export_amd import pgq
+
+    say("qgemm bf16 Y with a padded row stride; K = 0")
+    M, N, K = 77, 150, 96
+    x, codes, scales = _inputs(M, N, K, 6)
+    yb = torch.full((M, N + 5), 3.0, dtype=torch.bfloat16, device="cuda")
+    ops.qgemm(_bf16(x), torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda(),
+              out=yb[:, :N], out_dtype=torch.bfloat16)
+    y32 = ops.qgemm(_bf16(x), torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    b = yb[:, :N].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(b, _bf16_bits_of(y32.cpu().numpy()))
+    assert bool((yb[:, N:] == 3.0).all())              # nothing written past N
+    y0 = torch.full((M, N + 3), 7.0, dtype=torch.bfloat16, device="cuda")
+    rc = pgq.pgq_qgemm_bf16_ybf16(None, M, 0, 0, None, 0, None, N, y0.data_ptr(), N + 3,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert rc == pgq.PGQ_OK
+    torch.cuda.synchronize()
+    z = y0.view(torch.int16).cpu().numpy()
+    assert np.all(z[:, :N] == 0) and bool((y0[:, N:] == 7.0).all())   # +0, sign included
+
+
+def test_qgemm_ybf16_bench_shape_sampled_rows():
+    say("qgemm bf16 Y 16384 x 1584 x 528 sampled rows")
+    M, N, K = 16384, 1584, 528
+    x, codes, scales = _inputs(M, N, K, 19)
+    xd, cd, sd = _bf16(x), torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda()
+    y32 = ops.qgemm(xd, cd, sd)
+    y16 = ops.qgemm(xd, cd, sd, out_dtype=torch.bfloat16)
+    y16b = ops.qgemm(xd, cd, sd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    b = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(b, y16b.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.array_equal(b, _bf16_bits_of(y32.cpu().numpy()))
+    rows = np.r_[0:2, 126:131, 8000:8002, 16255:16258, 16382:16384]
+    ref, bound = oracle.qgemm_bf16(x[rows], codes, scales)
+    err = np.abs(oracle.bf16_to_f32(b[rows]).astype(np.float64) - ref)
+    assert np.all(err <= _ybf16_tol(ref, bound, K))
