@@ -201,3 +201,20 @@ def test_qgemm_ybf16_bench_shape_sampled_rows():
     ref, bound = oracle.qgemm_bf16(x[rows], codes, scales)
     err = np.abs(oracle.bf16_to_f32(b[rows]).astype(np.float64) - ref)
     assert np.all(err <= _ybf16_tol(ref, bound, K))
+
+
+def test_qgemm_ybf16_unaligned_rows_take_the_same_kernel():
+    """bf16 Y starting 2 bytes into a buffer, row stride odd: no 16-byte stores are possible, the
+    element-store path of the same kernel writes it, and it still equals bf16 of the fp32 Y (K a
+    multiple of 16 with 16-byte rows: the direct-to-LDS kernel for both)."""
+    say("qgemm bf16 Y at a 2-byte offset, odd row stride")
+    M, N, K = 300, 203, 160
+    x, codes, scales = _inputs(M, N, K, 23)
+    xd, cd, sd = _bf16(x), torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda()
+    yb = torch.full((M, N + 2), 5.0, dtype=torch.bfloat16, device="cuda")
+    ops.qgemm(xd, cd, sd, out=yb[:, 1:N + 1], out_dtype=torch.bfloat16)
+    y32 = ops.qgemm(xd, cd, sd)
+    torch.cuda.synchronize()
+    b = yb[:, 1:N + 1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(b, _bf16_bits_of(y32.cpu().numpy()))
+    assert bool((yb[:, 0] == 5.0).all()) and bool((yb[:, N + 1] == 5.0).all())
