@@ -684,7 +684,7 @@ def main() -> int:
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer is "
-              f"row-parallel within a GPU and this build runs no collectives)", file=sys.stderr)
+              f"row-parallel within a GPU; sharding over GPUs is not implemented)", file=sys.stderr)
         return 2
     steps = args.steps if args.steps is not None else DEFAULT_STEPS.get(args.mode, 1000)
     warmup = args.warmup if args.warmup is not None else DEFAULT_WARMUP.get(args.mode, 50)
