@@ -42,6 +42,10 @@ namespace pgq {
 namespace {
 
 constexpr int kFastRank = 8;     // ranks up to this use the iterated wave max
+// ranks 2 .. kTop2Rank first try each lane's two largest keys; that fails when a lane holds three
+// of the keys at or above the answer.  For keys in random places the expected number of such
+// triples is about C(r, 3) / 64^2: 0.14 at r = 16, 0.49 at r = 24.
+constexpr int kTop2Rank = 24;
 
 #define GLB __attribute__((address_space(1)))
 // lambdas of the row paths are inlined like the __forceinline__ functions around them (a call
@@ -338,24 +342,48 @@ __device__ __forceinline__ void radix_digit(HistPtr hist, uint32_t rem, int lane
     radix_digit_bins(h, rem, lane, digit, above);
 }
 
-// The k-th largest (1 <= k <= 64) of the 64 values the lanes hold: a lane whose value has fewer
-// than k values above it and at least k at or above it holds the answer.  All lanes active.
+// The k-th largest (1 <= k <= 64) of the 64 values the lanes hold: the largest t with at least k
+// values >= t (that count only falls as t grows), built bit by bit from the top with one ballot
+// per bit.  All lanes active.
 __device__ __forceinline__ uint32_t rank_select64(uint32_t v, uint32_t k)
 {
-    uint32_t gt = 0, ge = 0;
+    uint32_t t = 0;
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-        const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
-        gt += u > v ? 1u : 0u;
-        ge += u >= v ? 1u : 0u;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = t | (1u << b);
+        if ((uint32_t)__builtin_popcountll(__ballot(v >= c)) >= k) t = c;
     }
-    const uint64_t hit = __ballot(gt < k && k <= ge);
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)__builtin_ctzll(hit));
+    return t;
 }
 
 template <class Each>
 __device__ __forceinline__ uint32_t kth_largest(Each&& each, int64_t r, uint32_t* hist, int lane)
 {
+    if (r >= 2 && r <= kTop2Rank) {
+        // each lane's two largest keys.  t, the r-th largest of these 128 values (a lane with
+        // fewer than two elements offers 0, which is below every t > 0), is the row's r-th largest
+        // when no lane holds more than two keys >= t: then the keys >= t, and those > t, are the
+        // same in the row as among the lanes' two largest.  Otherwise one of the paths below.
+        uint32_t a = 0, b = 0;
+        each([&](uint32_t k, bool ok) PGQ_AI {
+            if (ok) {
+                const uint32_t lo = min(a, k);
+                a = max(a, k);
+                b = max(b, lo);
+            }
+        });
+        uint32_t t = 0;                        // bit by bit from the top, as in rank_select64
+#pragma unroll
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = t | (1u << bit);
+            const uint32_t n = (uint32_t)__builtin_popcountll(__ballot(a >= c)) +
+                               (uint32_t)__builtin_popcountll(__ballot(b >= c));
+            if (n >= (uint32_t)r) t = c;
+        }
+        uint32_t above = 0;
+        each([&](uint32_t k, bool ok) PGQ_AI { above += (ok && k >= t) ? 1u : 0u; });
+        if (__ballot(above > 2u) == 0) return t;
+    }
     if (r <= kFastRank) {
         // iterated maximum: strip the largest distinct magnitudes until r elements are covered.
         // One pass per round: the count of the current maximum m and the largest key below it.
