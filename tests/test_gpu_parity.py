@@ -429,6 +429,34 @@ def test_select_every_rank_path(cols):
         _check_rows(w, out, 31, num, den, f"select {cols} rank {rank}")
 
 
+@pytest.mark.parametrize("cols", [512, 528, 1536, 2000])
+def test_select_top_keys_sharing_lanes(cols):
+    """Ranks 2-25 from the top, with the largest keys placed where they share a lane: a run of
+    consecutive elements (one 16- or 32-byte slot), every 64th element (one lane of the
+    element-wise layouts), pairs of keys per slot (two per lane, the most the two-largest
+    path accepts), and copies of one value tying at the answer."""
+    rng = np.random.default_rng(cols + 7)
+    base = (rng.standard_normal((6, cols)) * 0.02).astype(np.float32)
+    w = base.copy()
+    big = (np.arange(30, 0, -1) * 0.05).astype(np.float32)
+    w[0, :8] = big[:8]                               # one run of consecutive elements
+    w[1, 0:64 * 6:64] = big[:6]                      # every 64th element
+    w[2, 8:16] = -big[:8]                            # a run of negatives
+    for k in range(12):                              # two keys per 4-element slot
+        w[3, 8 * k] = big[2 * k]
+        w[3, 8 * k + 1] = -big[2 * k + 1]
+    w[4, 0:64 * 10:64] = 0.75                        # ten copies of one key, one lane
+    w[4, 3:3 + 64 * 10:64] = 0.75                    # and ten in another
+    w[5, :4] = 0.75                                  # a tie inside one slot, more copies elsewhere
+    w[5, 100:1000:100] = 0.75 if cols > 900 else 0.5
+    for rank in [2, 3, 4, 5, 6, 9, 12, 16, 20, 24, 25]:
+        say(f"select lanes {w.shape[0]}x{cols} rank {rank}")
+        num, den = cols - rank + 1, cols
+        out = ops.quantize_rows(dev(w), bits=6, pct=(num, den))
+        torch.cuda.synchronize()
+        _check_rows(w, out, 31, num, den, f"select lanes {cols} rank {rank}")
+
+
 def test_edge_rows_and_status_bits():
     say("edge rows: zeros, spike, constant, grid, ties, tiny")
     n = 512
