@@ -21,7 +21,7 @@ constexpr int kPickGroups = 8;                // four-slot groups a thread keeps
 // the answer from below, so only the candidates at or above it can be it: they are gathered
 // (usually a few hundred) and each is ranked against all of them.  More than kPickBuf of them
 // (heavy ties) fall back to a radix select over the valid candidates.
-__device__ void cand_pick(const Desc* dp, GLB TState* S, uint32_t* sl, uint32_t* buf)
+__device__ __forceinline__ void cand_pick(const Desc* dp, GLB TState* S, uint32_t* sl, uint32_t* buf)
 {
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
