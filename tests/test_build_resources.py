@@ -64,3 +64,12 @@ def test_gemm_fits_without_scratch():
     res = _load()
     g = [v for k, v in res.items() if re.search(r"pgq_qgemm_kernel", k)]     # fp32 and bf16 Y
     assert len(g) == 2 and all(v["scratch"] == 0 and v["occupancy"] >= 2 for v in g), g
+
+
+def test_tensor_pick_is_one_inlined_kernel():
+    """The whole-tensor pick keeps its candidate ranking inline: compiled as an out-of-line call
+    it needed 12 bytes of scratch per lane and 102 VGPRs, and the pick took 12.0 instead of
+    10.9 us."""
+    res = _load()
+    p = [v for k, v in res.items() if "pgq_tensor_pick_kernel" in k]
+    assert len(p) == 1 and p[0]["scratch"] == 0 and p[0]["vgprs"] <= 80, p
